@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Throughput of the low-rank bottleneck block on one MI355X.
+
+A step is one forward + backward pass of the whole block (every product,
+the fused Online-RMSNorm statistics and scale, SiLU/SwiGLU and their
+recompute) over one batch of seeded synthetic input resident in HBM. The
+default workload is the LLaMA-2-7B-shaped low-rank SwiGLU MLP (T = 8192
+tokens, d = 4096, r = 1024, ffn = 11008, bf16 with fp32 accumulation).
+
+Prints one JSON line on stdout. Besides the contract fields it carries:
+  roofline      the dominant kernel's algorithmic TFLOP/s (per-launch flops /
+                average launch time from HIP events recorded around that
+                kernel on its launch stream during the timed steps), against
+                the bf16 dense MFMA peak, and its HBM traffic from committed
+                rocprofv3 counters when they match the current sources;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+                workload on this host (a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from rank_bottleneck_online_amd import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
+METRIC = "low-rank block fwd+bwd TFLOP/s (% bf16 MFMA peak) + tokens/s, 7B shape"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_bottleneck_online_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "boost_lrblock.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic flops (the method's own products, with its prescribed recompute)
+# ---------------------------------------------------------------------------
+
+def mlp_kernel_flops(T, d, r, ffn):
+    return {
+        "mlp_down1": 2 * T * d * 2 * r,
+        "mlp_up1_swiglu": 2 * 2 * T * r * ffn,
+        "mlp_down2": 2 * T * ffn * r,
+        "mlp_up2": 2 * T * r * d,
+        "mlp_ds2": 2 * T * d * r,
+        "mlp_dB2": 2 * r * d * T,
+        "mlp_dM": 2 * T * r * ffn,
+        "mlp_recompute_swiglu_bwd": 2 * 2 * T * r * ffn,
+        "mlp_dA2": 2 * ffn * r * T,
+        "mlp1_ds": 2 * 2 * T * ffn * r,
+        "mlp1_dB": 2 * 2 * r * ffn * T,
+        "mlp1_dA": 2 * d * 2 * r * T,
+        "mlp1_dx": 2 * T * 2 * r * d,
+    }
+
+
+def lrblock_kernel_flops(T, d, r, G, n, bwd=True):
+    f = {"lrblock_down": 2 * T * d * G * r, "lrblock_up": 2 * G * T * r * n}
+    if bwd:
+        f.update({"lrblock_ds": 2 * G * T * n * r, "lrblock_dB": 2 * G * r * n * T,
+                  "lrblock_dA": 2 * d * G * r * T, "lrblock_dx": 2 * T * G * r * d})
+    return f
+
+
+def btp_kernel_flops(T, r, ds):
+    return {"btp_u": 2 * T * r * ds, "btp_p": 2 * T * ds * r, "btp_e": 2 * T * r * ds,
+            "btp_u_bwd": 2 * T * r * ds, "btp_dA": 2 * ds * r * T, "btp_dB": 2 * r * ds * T,
+            "btp_dz": 2 * T * ds * r}
+
+
+# ---------------------------------------------------------------------------
+# Workloads: inputs on the GPU, a step closure, flops, and an oracle sample
+# ---------------------------------------------------------------------------
+
+class Workload:
+    def __init__(self, name):
+        import torch
+        from rank_bottleneck_online_amd import binding as B
+        self.name = name
+        self.w = w = synth.WORKLOADS[name]
+        self.kind = w["kind"]
+        self.dtype = w["dtype"]
+        self.B = B
+        self.torch = torch
+        self.bwd = name != "llama2_1b_qkv_fwd"
+        self.acts = ["silu"]
+        if self.kind == "layerset":
+            self.acts = ["silu", "identity"]
+        self._setup()
+
+    def dev(self, a):
+        return self.B.upload(a, self.dtype)
+
+    def _setup(self):
+        B, torch, w = self.B, self.torch, self.w
+        dt = B.DT_BF16 if self.dtype == "bf16" else B.DT_F32
+        if self.kind == "lrmlp":
+            T, d, r, ffn = w["T"], w["d"], w["r"], w["ffn"]
+            inp = synth.lrmlp_inputs(T, d, r, ffn, dtype=self.dtype, seed=0)
+            t = {k: self.dev(v) for k, v in inp.items()}
+            desc = B.lrmlp_desc(T, d, r, ffn, dt)
+            ws_f = torch.empty(B.lrmlp_workspace_size(desc, False), dtype=torch.uint8, device="cuda")
+            ws_b = torch.empty(B.lrmlp_workspace_size(desc, True), dtype=torch.uint8, device="cuda")
+            fo = B.lrmlp_fwd(t["x"], t["g"], t["A1_cat"], t["B1"], t["A2"], t["B2"], ws=ws_f)
+            bo = B.lrmlp_bwd(t["x"], t["g"], t["A1_cat"], t["B1"], t["A2"], t["B2"], *fo[1:], t["dY"], ws=ws_b)
+            args = [t[k] for k in ("x", "g", "A1_cat", "B1", "A2", "B2")]
+
+            def step():
+                B.lrmlp_fwd(*args, out=fo, ws=ws_f)
+                B.lrmlp_bwd(*args, *fo[1:], t["dY"], out=bo, ws=ws_b)
+
+            self.step = step
+            self.tokens = T
+            self.kflops = mlp_kernel_flops(T, d, r, ffn)
+            self.shape = dict(T=T, d=d, r=r, ffn=ffn)
+        elif self.kind == "lrblock":
+            T, d, r, G, n = w["T"], w["d"], w["r"], w["G"], w["d_out"]
+            inp = synth.lrblock_inputs(T, d, r, G, n, dtype=self.dtype, seed=0)
+            t = {k: self.dev(v) for k, v in inp.items()}
+            desc = B.lrblock_desc(T, d, r, G, n, dt)
+            ws_f = torch.empty(B.lrblock_workspace_size(desc, False), dtype=torch.uint8, device="cuda")
+            ws_b = torch.empty(B.lrblock_workspace_size(desc, True), dtype=torch.uint8, device="cuda")
+            fo = B.lrblock_fwd(t["x"], t["g"], t["A_cat"], t["B"], ws=ws_f)
+            bo = B.lrblock_bwd(t["x"], t["g"], t["A_cat"], t["B"], fo[1], fo[2], t["dY"], ws=ws_b) \
+                if self.bwd else None
+
+            def step():
+                B.lrblock_fwd(t["x"], t["g"], t["A_cat"], t["B"], out=fo, ws=ws_f)
+                if self.bwd:
+                    B.lrblock_bwd(t["x"], t["g"], t["A_cat"], t["B"], fo[1], fo[2], t["dY"], out=bo, ws=ws_b)
+
+            self.step = step
+            self.tokens = T
+            self.kflops = lrblock_kernel_flops(T, d, r, G, n, self.bwd)
+            self.shape = dict(T=T, d=d, r=r, G=G, d_out=n)
+        elif self.kind == "btp":
+            T, r, D, P = w["T"], w["r"], w["d_global"], w["P"]
+            inp = synth.btp_inputs(T, r, D, P, dtype=self.dtype, seed=0)
+            sh = synth.btp_shard(inp, 0, P)
+            t = {k: self.dev(sh[k]) for k in ("z", "B_s", "g_s", "A_s", "dp")}
+            ds = self.B.upload(sh["ds"], "f32")
+            desc = B.btp_desc(T, r, D // P, dt)
+            ws_f = torch.empty(B.btp_workspace_size(desc, False), dtype=torch.uint8, device="cuda")
+            ws_b = torch.empty(B.btp_workspace_size(desc, True), dtype=torch.uint8, device="cuda")
+            args = [t[k] for k in ("z", "B_s", "g_s", "A_s")]
+            fo = B.btp_share_fwd(*args, ws=ws_f)
+            bo = B.btp_share_bwd(*args, t["dp"], ds, ws=ws_b)
+
+            def step():
+                B.btp_share_fwd(*args, out=fo, ws=ws_f)
+                B.btp_share_bwd(*args, t["dp"], ds, out=bo, ws=ws_b)
+
+            self.step = step
+            self.tokens = T
+            self.kflops = btp_kernel_flops(T, r, D // P)
+            self.shape = dict(T=T, r=r, d_shard=D // P, d_global=D, tp=P)
+        elif self.kind == "layerset":
+            T, d, r, ffn = w["T"], w["d"], w["r"], w["ffn"]
+            inp = synth.layerset_inputs(T, d, r, ffn, dtype=self.dtype, seed=0)
+            q = {k: self.dev(v) for k, v in inp["qkv"].items()}
+            o = {k: self.dev(v) for k, v in inp["o"].items()}
+            m = {k: self.dev(v) for k, v in inp["mlp"].items()}
+            dq = B.lrblock_desc(T, d, r, 3, d, dt)
+            do = B.lrblock_desc(T, d, r, 1, d, dt, norm=False)
+            dm = B.lrmlp_desc(T, d, r, ffn, dt)
+            sizes = [B.lrblock_workspace_size(dq, 0), B.lrblock_workspace_size(dq, 1),
+                     B.lrblock_workspace_size(do, 0), B.lrblock_workspace_size(do, 1),
+                     B.lrmlp_workspace_size(dm, 0), B.lrmlp_workspace_size(dm, 1)]
+            ws = torch.empty(max(sizes), dtype=torch.uint8, device="cuda")
+            state = {}
+            for act in self.acts:
+                qf = B.lrblock_fwd(q["x"], q["g"], q["A_cat"], q["B"], act=act, ws=ws)
+                qb = B.lrblock_bwd(q["x"], q["g"], q["A_cat"], q["B"], qf[1], qf[2], q["dY"], act=act, ws=ws)
+                of = B.lrblock_fwd(o["x"], None, o["A_cat"], o["B"], act=act, norm=False, ws=ws)
+                ob = B.lrblock_bwd(o["x"], None, o["A_cat"], o["B"], of[1], None, o["dY"], act=act, norm=False,
+                                   ws=ws)
+                ma = [m[k] for k in ("x", "g", "A1_cat", "B1", "A2", "B2")]
+                mf = B.lrmlp_fwd(*ma, act=act, ws=ws)
+                mb = B.lrmlp_bwd(*ma, *mf[1:], m["dY"], act=act, ws=ws)
+                state[act] = (qf, qb, of, ob, mf, mb)
+            self.act = self.acts[0]
+
+            def step():
+                act = self.act
+                qf, qb, of, ob, mf, mb = state[act]
+                ma = [m[k] for k in ("x", "g", "A1_cat", "B1", "A2", "B2")]
+                B.lrblock_fwd(q["x"], q["g"], q["A_cat"], q["B"], act=act, out=qf, ws=ws)
+                B.lrblock_bwd(q["x"], q["g"], q["A_cat"], q["B"], qf[1], qf[2], q["dY"], act=act, out=qb, ws=ws)
+                B.lrblock_fwd(o["x"], None, o["A_cat"], o["B"], act=act, norm=False, out=of, ws=ws)
+                B.lrblock_bwd(o["x"], None, o["A_cat"], o["B"], of[1], None, o["dY"], act=act, norm=False,
+                              out=ob, ws=ws)
+                B.lrmlp_fwd(*ma, act=act, out=mf, ws=ws)
+                B.lrmlp_bwd(*ma, *mf[1:], m["dY"], act=act, out=mb, ws=ws)
+
+            self.step = step
+            self.tokens = T
+            # QKV and O launches share the lrblock_* labels with different
+            # per-launch flops, so only the MLP kernels get a roofline here.
+            self.kflops = mlp_kernel_flops(T, d, r, ffn)
+            self.shape = dict(T=T, d=d, r=r, ffn=ffn)
+        self.flops = self.step_flops()
+
+    def step_flops(self) -> float:
+        w = self.w
+        if self.kind == "lrmlp":
+            return float(sum(mlp_kernel_flops(w["T"], w["d"], w["r"], w["ffn"]).values()))
+        if self.kind == "lrblock":
+            return float(sum(lrblock_kernel_flops(w["T"], w["d"], w["r"], w["G"], w["d_out"], self.bwd).values()))
+        if self.kind == "btp":
+            return float(sum(btp_kernel_flops(w["T"], w["r"], w["d_global"] // w["P"]).values()))
+        T, d, r, ffn = w["T"], w["d"], w["r"], w["ffn"]
+        return float(sum(lrblock_kernel_flops(T, d, r, 3, d).values()) +
+                     sum(lrblock_kernel_flops(T, d, r, 1, d).values()) +
+                     sum(mlp_kernel_flops(T, d, r, ffn).values()))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(name, target_s):
+    import oracle  # test infrastructure; used here only for the CPU baseline leg
+    w = synth.WORKLOADS[name]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+
+    def run(Ts):
+        if w["kind"] == "lrmlp":
+            inp = synth.lrmlp_inputs(Ts, w["d"], w["r"], w["ffn"], dtype=w["dtype"], seed=0)
+            a = [inp[k] for k in ("x", "g", "A1_cat", "B1", "A2", "B2")]
+            t0 = time.perf_counter()
+            oracle.lrmlp_forward(*a)
+            oracle.lrmlp_backward(*a, inp["dY"])
+            dt = time.perf_counter() - t0
+            return dt, float(sum(mlp_kernel_flops(Ts, w["d"], w["r"], w["ffn"]).values()))
+        if w["kind"] == "lrblock":
+            inp = synth.lrblock_inputs(Ts, w["d"], w["r"], w["G"], w["d_out"], dtype=w["dtype"], seed=0)
+            a = [inp[k] for k in ("x", "g", "A_cat", "B")]
+            bwd = name != "llama2_1b_qkv_fwd"
+            t0 = time.perf_counter()
+            oracle.lrblock_forward(*a)
+            if bwd:
+                oracle.lrblock_backward(*a, inp["dY"])
+            dt = time.perf_counter() - t0
+            return dt, float(sum(lrblock_kernel_flops(Ts, w["d"], w["r"], w["G"], w["d_out"], bwd).values()))
+        if w["kind"] == "btp":
+            inp = synth.btp_inputs(Ts, w["r"], w["d_global"], w["P"], dtype=w["dtype"], seed=0)
+            sh = synth.btp_shard(inp, 0, w["P"])
+            a = [sh[k] for k in ("z", "B_s", "g_s", "A_s")]
+            t0 = time.perf_counter()
+            oracle.btp_share_forward(*a)
+            oracle.btp_share_backward(*a, sh["dp"], sh["ds"])
+            dt = time.perf_counter() - t0
+            return dt, float(sum(btp_kernel_flops(Ts, w["r"], w["d_global"] // w["P"]).values()))
+        inp = synth.layerset_inputs(Ts, w["d"], w["r"], w["ffn"], dtype=w["dtype"], seed=0)
+        t0 = time.perf_counter()
+        q, o, m = inp["qkv"], inp["o"], inp["mlp"]
+        oracle.lrblock_backward(q["x"], q["g"], q["A_cat"], q["B"], q["dY"])
+        oracle.lrblock_backward(o["x"], None, o["A_cat"], o["B"], o["dY"], norm=False)
+        ma = [m[k] for k in ("x", "g", "A1_cat", "B1", "A2", "B2")]
+        oracle.lrmlp_backward(*ma, m["dY"])
+        dt = time.perf_counter() - t0
+        T, d, r, ffn = Ts, w["d"], w["r"], w["ffn"]
+        fl = (sum(lrblock_kernel_flops(T, d, r, 3, d).values()) + sum(lrblock_kernel_flops(T, d, r, 1, d).values())
+              + sum(mlp_kernel_flops(T, d, r, ffn).values()))
+        return dt, float(fl)
+
+    T = w["T"]
+    probe = min(128, T)
+    dt, _ = run(probe)
+    Ts = int(min(T, max(probe, probe * target_s / max(dt, 1e-3))))
+    Ts = max(64, Ts // 64 * 64) if T >= 64 else T
+    dt, fl = run(Ts)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, fwd+bwd of the first {Ts} of {T} tokens of the same workload "
+                      f"(algorithmic flops scaled to the sample), {dt:.1f} s",
+            "tokens_per_s": Ts / dt}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama2_7b_mlp", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--act", default=None, help="bottleneck activation for the layer set (silu|identity)")
+    ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharded design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    from rank_bottleneck_online_amd import binding as B
+    B.lib()
+
+    wl = Workload(args.workload)
+    if args.act and wl.kind == "layerset":
+        wl.act = args.act
+    log(f"workload {args.workload} {wl.shape}; step flops {wl.flops / 1e9:.1f} GF")
+
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    # Which kernel dominates the step (untimed discovery pass).
+    B.profiler_enable(None, 4096)
+    wl.step()
+    rep = B.profiler_report()
+    B.profiler_disable()
+    per_kernel = {k: v[1] for k, v in rep.items()}
+    dom = max(per_kernel, key=per_kernel.get)
+    log("kernel times in one step (ms):", json.dumps({k: round(v, 4) for k, v in
+                                                       sorted(per_kernel.items(), key=lambda kv: -kv[1])}))
+
+    # Timed region: K steps, HIP events around the dominant kernel's launches.
+    B.profiler_enable(dom, 64 * max(1, args.steps))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        wl.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    rep = B.profiler_report()
+    B.profiler_disable()
+
+    cnt, tot = rep.get(dom, (0, 0.0))
+    avg_ms = tot / max(cnt, 1)
+    launches_per_step = cnt / args.steps
+    dom_flops = wl.kflops.get(dom)
+    value = wl.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    roofline = None
+    if dom_flops:
+        achieved = dom_flops / (avg_ms * 1e-3) / 1e12
+        traffic = None
+        if os.path.exists(TRAFFIC_JSON):
+            tj = json.load(open(TRAFFIC_JSON))
+            if tj.get("source_digest") == source_digest() and tj.get("workload") == args.workload:
+                k = tj.get("kernels", {}).get(dom)
+                if k:
+                    traffic = k["fetch_bytes"] + k["write_bytes"]
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+                    "kernel_avg_ms": round(avg_ms, 5), "launches_per_step": launches_per_step,
+                    "algorithmic_gflop_per_launch": round(dom_flops / 1e9, 3)}
+
+    cpu = None
+    if args.cpu_baseline == "on":
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded Gaussian, LLaMA-2 shapes)",
+        "config": {"workload": args.workload, **wl.shape, **({"act": wl.act} if wl.kind == "layerset" else {})},
+        "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "algorithmic_gflop_per_step": round(wl.flops / 1e9, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

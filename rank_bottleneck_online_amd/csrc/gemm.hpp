@@ -1,0 +1,510 @@
+// GEMM core for gfx950 (CDNA4): MFMA tiles staged through LDS.
+//
+// C[M,N] (+)= A[M,K] @ B[K,N] with fp32 accumulation, for the products of
+// the low-rank bottleneck block (down projections, batched up projections,
+// their backward products and the weight gradients with K = tokens).
+//
+// Element types: bfloat16 (v_mfma_f32_32x32x16_bf16) and fp32
+// (v_mfma_f32_32x32x2_f32). Both use the 32x32 accumulator layout: lane l
+// holds C[8*(v/4) + 4*(l/32) + v%4][l%32] for v = 0..15.
+//
+// Operand layouts. The MFMA wants both operands with K contiguous per lane.
+//   A "KC": element (m,k) at m*ld + k  (activations x, dY, S, ...)
+//   A "MC": element (m,k) at k*ld + m  (transposed activations, K = tokens)
+//   B "KC": element (k,n) at n*ld + k  (a weight used transposed)
+//   B "NC": element (k,n) at k*ld + n  (a weight in [in,out] layout, or an
+//           activation when K = tokens)
+// KC operands are copied to LDS in 16-byte chunks. MC/NC operands are loaded
+// as VEC x VEC blocks (VEC elements per 16 bytes), transposed in registers,
+// and written K-contiguous, so the MFMA loop only ever sees one LDS layout.
+//
+// LDS layout: each staged tile row holds 128 bytes of K (BK = 64 bf16 or
+// 32 fp32). 16-byte chunk c of row m lives at chunk c ^ ((m ^ (m>>3)) & 7):
+// MFMA fragment reads (8 consecutive rows, same chunk) and transposed
+// writes (rows 8 apart, same chunk) both hit 8 distinct chunks.
+//
+// Global loads use buffer instructions with a per-operand byte range, so
+// every read past the end of a tensor returns zero: rows past T and the
+// K tail of K = tokens products need no branches. Reads past M or N inside
+// the tensor only feed accumulator rows/columns that the epilogue masks.
+//
+// Pipelining: two LDS stages; the next K slab is fetched into registers while
+// the MFMAs consume the current stage, then written to the other stage; one
+// barrier per K step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace rbo {
+
+typedef __bf16 bf16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRowBytes = 128;  // bytes of K per staged tile row
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = B..E-1. Used
+// wherever accumulator registers are indexed, so that no index is ever a
+// runtime value (a runtime index would move the accumulators to scratch).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ lds_swz(row)) << 4);
+}
+
+// ---------------------------------------------------------------------------
+// Scalar conversions
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<bf16> {
+  static __device__ __forceinline__ float to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    bf16 h = static_cast<bf16>(v);  // round to nearest even
+    static_cast<bf16*>(p)[i] = h;
+  }
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return to_f32(static_cast<const uint16_t*>(p)[i]);
+  }
+};
+template <> struct Elem<float> {
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA traits
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16> {
+  static constexpr int KI = 16;  // K per instruction
+  static constexpr int KL = 8;   // contiguous K per lane
+  typedef bf16x8 Frag;
+  static __device__ __forceinline__ Frag read(const char* tile, int row, int k) {
+    return *reinterpret_cast<const bf16x8*>(tile + lds_off(row, k >> 3));
+  }
+  static __device__ __forceinline__ floatx16 mma(Frag a, Frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int KI = 2;
+  static constexpr int KL = 1;
+  typedef float Frag;
+  static __device__ __forceinline__ Frag read(const char* tile, int row, int k) {
+    return *reinterpret_cast<const float*>(tile + lds_off(row, k >> 2) + ((k & 3) << 2));
+  }
+  static __device__ __forceinline__ floatx16 mma(Frag a, Frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Tile configuration
+// ---------------------------------------------------------------------------
+template <typename T_, int BM_, int BN_, int WM_, int WN_, bool AKC_, bool BKC_, int NACC_>
+struct Cfg {
+  typedef T_ T;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NACC = NACC_;
+  static constexpr bool AKC = AKC_, BKC = BKC_;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int ES = sizeof(T);
+  static constexpr int VEC = 16 / ES;
+  static constexpr int BK = kRowBytes / ES;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int PIPE_BYTES = 2 * STAGE_BYTES;
+  // After the pipeline: per-row and per-column fp32 vectors for epilogues.
+  static constexpr int VEC_BYTES = (BM + BN) * 4;
+  static constexpr int LDS_BYTES = PIPE_BYTES + VEC_BYTES;
+  static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA block");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+};
+
+// ---------------------------------------------------------------------------
+// Operands and problem geometry (passed by value to kernels)
+// ---------------------------------------------------------------------------
+struct Operand {
+  const void* ptr;        // batch-0 base
+  int64_t ld;             // elements between consecutive memory rows
+  int64_t batch_stride;   // elements between consecutive batches
+  int64_t extent;         // bytes from a batch base to the end of its valid data
+};
+
+struct GemmGeom {
+  int M, N, K;
+  int batch;     // independent problems
+  int splits;    // K splits (partial results go to separate outputs)
+  int k_split;   // K range per split, a multiple of BK
+  int tiles_m, tiles_n;
+};
+
+struct GemmOps {
+  Operand a[2], b[2];  // one pair per accumulator (NACC <= 2)
+};
+
+// Per-tile context handed to the epilogue.
+struct TileCtx {
+  int m0, n0;        // tile origin in the output
+  int tm, tn;        // tile indices
+  int bidx, split;   // batch index, K-split index
+  int prob;          // bidx * splits + split
+  int M, N;
+  int t, lane, wm, wn;
+  char* smem;        // pipeline LDS, free for epilogue scratch
+  float* rowv;       // BM fp32 in LDS (row statistics from the A loader)
+  float* colv;       // BN fp32 in LDS
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  int64_t n = bytes < 0 ? 0 : bytes;
+  if (n > 0x7fffffffLL) n = 0x7fffffffLL;
+  // dword3 0x00020000: raw (untyped) buffer, 32-bit data format, as used for
+  // gfx9-family buffer resources.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Operand loader: one K slab (ROWS x BK) of one operand per call.
+// ---------------------------------------------------------------------------
+template <class C, int ROWS, bool KC, bool FROM_TOP, bool ROWSUMSQ>
+struct Loader {
+  static constexpr int VEC = C::VEC;
+  // KC: ROWS*8 chunks; thread t takes chunk t&7 of rows (t>>3) + u*(NT/8).
+  static constexpr int KC_UNITS = (ROWS * 8) / C::NT;
+  // transposed: (BK/VEC) x (ROWS/VEC) blocks of VEC x VEC elements.
+  static constexpr int BLOCKS = (C::BK / VEC) * (ROWS / VEC);
+  static constexpr int T_UNITS = cdiv(BLOCKS, C::NT);
+  static constexpr int NREG = KC ? KC_UNITS : T_UNITS * VEC;
+  static_assert(!KC || (ROWS * 8) % C::NT == 0, "KC loader: ROWS*8 must divide by NT");
+  static_assert(!KC || KC_UNITS >= 1, "KC loader: too few rows");
+
+  u32x4 r[NREG];
+  float ss[KC ? KC_UNITS : 1];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int u = 0; u < (KC ? KC_UNITS : 1); ++u) ss[u] = 0.f;
+  }
+
+  // Issue the global reads of the slab starting at column/row k0.
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int k0, int t) {
+    if constexpr (KC) {
+      const int c = t & 7;
+#pragma unroll
+      for (int u = 0; u < KC_UNITS; ++u) {
+        const int row = (t >> 3) + u * (C::NT / 8);
+        const uint32_t off = (uint32_t)(row * ld_bytes) + (uint32_t)((k0 + c * VEC) * C::ES);
+        r[u] = buf_load16(rs, off);
+      }
+    } else {
+      const int tt = FROM_TOP ? (C::NT - 1 - t) : t;
+#pragma unroll
+      for (int u = 0; u < T_UNITS; ++u) {
+        const int b = u * C::NT + tt;
+        if (BLOCKS % C::NT == 0 || b < BLOCKS) {
+          const int mb = b % (ROWS / VEC), kb = b / (ROWS / VEC);
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) {
+            const int k = k0 + kb * VEC + j;
+            const uint32_t off = (uint32_t)((int64_t)k * ld_bytes) + (uint32_t)(mb * 16);
+            r[u * VEC + j] = buf_load16(rs, off);
+          }
+        }
+      }
+    }
+  }
+
+  // Write the fetched slab into an LDS tile (K-contiguous rows).
+  __device__ __forceinline__ void store(char* tile, int t) {
+    if constexpr (KC) {
+      const int c = t & 7;
+#pragma unroll
+      for (int u = 0; u < KC_UNITS; ++u) {
+        const int row = (t >> 3) + u * (C::NT / 8);
+        *reinterpret_cast<u32x4*>(tile + lds_off(row, c)) = r[u];
+        if constexpr (ROWSUMSQ) ss[u] = sumsq16(r[u], ss[u]);
+      }
+    } else {
+      const int tt = FROM_TOP ? (C::NT - 1 - t) : t;
+#pragma unroll
+      for (int u = 0; u < T_UNITS; ++u) {
+        const int b = u * C::NT + tt;
+        if (BLOCKS % C::NT == 0 || b < BLOCKS) {
+          const int mb = b % (ROWS / VEC), kb = b / (ROWS / VEC);
+          u32x4 o[VEC];
+          transpose(&r[u * VEC], o);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i)
+            *reinterpret_cast<u32x4*>(tile + lds_off(mb * VEC + i, kb)) = o[i];
+        }
+      }
+    }
+  }
+
+  // Sum of squares of the 16 bytes of one chunk, accumulated into acc.
+  static __device__ __forceinline__ float sumsq16(u32x4 v, float acc) {
+    if constexpr (C::ES == 2) {
+      // The words are copied to scalars first: bit-casting a vector element
+      // selected by the loop index straight into the dot2 builtin makes this
+      // compiler read word 0 four times.
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const bf16x2 p = __builtin_bit_cast(bf16x2, wv[w]);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __uint_as_float(v[w]);
+        acc = __builtin_fmaf(f, f, acc);
+      }
+    }
+    return acc;
+  }
+
+  // in[j] holds VEC elements (m = 0..VEC-1) of K row j; out[i] gets the VEC
+  // K values of m = i.
+  static __device__ __forceinline__ void transpose(const u32x4* in, u32x4* out) {
+    if constexpr (C::ES == 2) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t x = in[2 * p][i >> 1], y = in[2 * p + 1][i >> 1];
+          out[i][p] = (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) out[i][p] = in[p][i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Block -> tile mapping. Workgroups are handed to the 8 XCDs round-robin;
+// the remap gives each XCD a contiguous range of logical tiles, and tiles are
+// walked in groups of 8 tile rows so neighbours share A rows and B columns in
+// that XCD's L2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int q = nb >> 3, rem = nb & 7, x = b & 7;
+  return x * q + (x < rem ? x : rem) + (b >> 3);
+}
+
+__device__ __forceinline__ void group_tile(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int gid = tile / per_group;
+  const int first = gid * GROUP;
+  const int gsz = (tiles_m - first) < GROUP ? (tiles_m - first) : GROUP;
+  const int in = tile - gid * per_group;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+template <class C, class E>
+__global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, typename E::Args ea) {
+  typedef typename C::T T;
+  typedef Mfma<T> MF;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr bool RSS = E::kRowSumsq;
+  static_assert(!RSS || C::AKC, "row statistics need a K-contiguous A");
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tiles = g.tiles_m * g.tiles_n;
+  const int prob = bid / tiles;
+  int tm, tn;
+  group_tile(bid - prob * tiles, g.tiles_m, g.tiles_n, tm, tn);
+  const int split = prob % g.splits, bidx = prob / g.splits;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int kbeg = split * g.k_split;
+  const int kend = (g.K - kbeg) < g.k_split ? g.K : kbeg + g.k_split;
+  const int KT = cdiv(kend - kbeg, C::BK);
+
+  floatx16 acc[C::NACC][C::FM][C::FN];
+#pragma unroll
+  for (int p = 0; p < C::NACC; ++p)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[p][i][j][v] = 0.f;
+
+  Loader<C, C::BM, C::AKC, false, RSS> la;
+  Loader<C, C::BN, C::BKC, true, false> lb;
+  la.init();
+
+#pragma unroll
+  for (int p = 0; p < C::NACC; ++p) {
+    const Operand& A = ops.a[p];
+    const Operand& B = ops.b[p];
+    // Rebase each operand on this tile so 32-bit buffer offsets suffice.
+    const int64_t a_off = (int64_t)bidx * A.batch_stride * C::ES +
+                          (C::AKC ? (int64_t)m0 * A.ld * C::ES : (int64_t)m0 * C::ES);
+    const int64_t b_off = (int64_t)bidx * B.batch_stride * C::ES +
+                          (C::BKC ? (int64_t)n0 * B.ld * C::ES : (int64_t)n0 * C::ES);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(static_cast<const char*>(A.ptr) + a_off, A.extent - ((int64_t)m0 * (C::AKC ? A.ld : 1) * C::ES));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(static_cast<const char*>(B.ptr) + b_off, B.extent - ((int64_t)n0 * (C::BKC ? B.ld : 1) * C::ES));
+    const int64_t lda_b = A.ld * C::ES, ldb_b = B.ld * C::ES;
+
+    la.fetch(ra, lda_b, kbeg, t);
+    lb.fetch(rb, ldb_b, kbeg, t);
+    la.store(smem, t);
+    lb.store(smem + C::A_BYTES, t);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < KT;
+      if (more) {
+        la.fetch(ra, lda_b, kbeg + (kt + 1) * C::BK, t);
+        lb.fetch(rb, ldb_b, kbeg + (kt + 1) * C::BK, t);
+      }
+      const char* As = smem + cur * C::STAGE_BYTES;
+      const char* Bs = As + C::A_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < C::BK / MF::KI; ++kk) {
+        const int k = kk * MF::KI + (lane >> 5) * MF::KL;
+        typename MF::Frag fa[C::FM], fb[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) fa[i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), k);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) fb[j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), k);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) acc[p][i][j] = MF::mma(fa[i], fb[j], acc[p][i][j]);
+      }
+      if (more) {
+        char* nx = smem + (cur ^ 1) * C::STAGE_BYTES;
+        la.store(nx, t);
+        lb.store(nx + C::A_BYTES, t);
+      }
+      __syncthreads();
+    }
+  }
+
+  float* rowv = reinterpret_cast<float*>(smem + C::PIPE_BYTES);
+  float* colv = rowv + C::BM;
+  if constexpr (RSS) {
+    // Row sums of squares of A (the Online-RMSNorm statistic): the 8 lanes
+    // holding the 8 chunks of a row reduce, lane 0 of the 8 publishes.
+#pragma unroll
+    for (int u = 0; u < decltype(la)::KC_UNITS; ++u) {
+      float s = la.ss[u];
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      if ((t & 7) == 0) rowv[(t >> 3) + u * (C::NT / 8)] = s;
+    }
+    __syncthreads();
+  }
+
+  TileCtx c;
+  c.m0 = m0; c.n0 = n0; c.tm = tm; c.tn = tn; c.bidx = bidx; c.split = split; c.prob = prob;
+  c.M = g.M; c.N = g.N; c.t = t; c.lane = lane; c.wm = wm; c.wn = wn;
+  c.smem = smem; c.rowv = rowv; c.colv = colv;
+  E::template run<C>(acc, c, ea);
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue helpers over the accumulator layout
+// ---------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ int acc_row(const TileCtx& c, int i, int v) {
+  return c.wm * C::WTM + i * 32 + (v >> 2) * 8 + (c.lane >> 5) * 4 + (v & 3);
+}
+template <class C>
+__device__ __forceinline__ int acc_col(const TileCtx& c, int j) {
+  return c.wn * C::WTN + j * 32 + (c.lane & 31);
+}
+
+// part[i][v] holds this lane's partial for tile row acc_row(i, v) summed over
+// its own columns. On return out[r] (LDS, r < BM) holds the sum over all BN
+// columns of the tile, in a fixed order. Uses the pipeline LDS as scratch.
+template <class C>
+__device__ __forceinline__ void tile_row_sum(const TileCtx& c, float (&part)[C::FM][16], float* out) {
+  float* scr = reinterpret_cast<float*>(c.smem);  // [WN][BM]
+  static_for<0, C::FM>([&](auto i) {
+    static_for<0, 16>([&](auto v) {
+      float s = part[i][v];
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      s += __shfl_xor(s, 8);
+      s += __shfl_xor(s, 16);
+      if ((c.lane & 31) == 0) scr[c.wn * C::BM + acc_row<C>(c, i, v)] = s;
+    });
+  });
+  __syncthreads();
+  for (int r = c.t; r < C::BM; r += C::NT) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::WN; ++w) s += scr[w * C::BM + r];
+    out[r] = s;
+  }
+  __syncthreads();
+}
+
+// part[j] holds this lane's partial for tile column acc_col(j) summed over
+// its own rows. On return out[n] (LDS, n < BN) holds the column sum over all
+// BM rows of the tile, in a fixed order.
+template <class C>
+__device__ __forceinline__ void tile_col_sum(const TileCtx& c, float (&part)[C::FN], float* out) {
+  float* scr = reinterpret_cast<float*>(c.smem);  // [WM][BN]
+  static_for<0, C::FN>([&](auto j) {
+    const float s = part[j] + __shfl_xor(part[j], 32);
+    if (c.lane < 32) scr[c.wm * C::BN + acc_col<C>(c, j)] = s;
+  });
+  __syncthreads();
+  for (int n = c.t; n < C::BN; n += C::NT) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::WM; ++w) s += scr[w * C::BN + n];
+    out[n] = s;
+  }
+  __syncthreads();
+}
+
+}  // namespace rbo

@@ -1,0 +1,182 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments before anything is launched (CPU only: no call here
+reaches a device API)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_bottleneck_online_amd import build as rbo_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "boost_lrblock.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not os.path.exists(rbo_build.LIB_PATH):
+        rbo_build.build()
+    from rank_bottleneck_online_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(boost_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("boost_lrblock_fwd", "boost_lrblock_bwd", "boost_lrmlp_fwd", "boost_lrmlp_bwd",
+              "boost_btp_share_fwd", "boost_btp_share_bwd", "boost_status_string",
+              "boost_last_error_detail", "boost_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    L = B.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    # and the binding declares a signature for every one of them
+    assert set(declared_functions()) <= set(B._SIGS)
+
+
+def test_abi_version_and_status_strings(B):
+    L = B.lib()
+    assert L.boost_abi_version() == 1
+    for code, name in [(0, "BOOST_OK"), (1, "BOOST_ERR_INVALID_VALUE"), (2, "BOOST_ERR_UNSUPPORTED"),
+                       (3, "BOOST_ERR_MISALIGNED"), (4, "BOOST_ERR_ALIASING"), (5, "BOOST_ERR_WORKSPACE"),
+                       (6, "BOOST_ERR_VERSION"), (7, "BOOST_ERR_LAUNCH")]:
+        assert L.boost_status_string(code).decode() == name
+    assert L.boost_status_string(99).decode() == "BOOST_ERR_UNKNOWN"
+
+
+# Fake, 256-byte aligned, non-overlapping "device" addresses: validation only
+# compares them, it never dereferences them.
+class Fake:
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes):
+        p = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+
+
+def lrblock_call(B, desc, fwd=True, mutate=None, ws_bytes=None):
+    L = B.lib()
+    T, d, r, G, n = desc.T, desc.d, desc.r, desc.G, desc.d_out
+    es = 4 if desc.dtype == B.DT_F32 else 2
+    f = Fake()
+    try:
+        need = B.lrblock_workspace_size(desc, not fwd)
+    except B.BoostError:
+        need = 1024  # the descriptor itself is invalid; the call must fail before the workspace check
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    if fwd:
+        args = dict(x=f(T * d * es), g=f(d * es), A=f(d * G * r * es), B=f(G * r * n * es), Y=f(G * T * n * es),
+                    H=f(T * G * r * 4), s=f(T * 4), ws=f(max(ws_bytes, 1)))
+        if mutate:
+            mutate(args)
+        return L.boost_lrblock_fwd(ctypes.byref(desc), args["x"], args["g"], args["A"], args["B"], args["Y"],
+                                   args["H"], args["s"], args["ws"], ws_bytes, None)
+    args = dict(x=f(T * d * es), g=f(d * es), A=f(d * G * r * es), B=f(G * r * n * es), H=f(T * G * r * 4),
+                s=f(T * 4), dY=f(G * T * n * es), dx=f(T * d * es), dg=f(d * 4), dA=f(d * G * r * 4),
+                dB=f(G * r * n * 4), ws=f(max(ws_bytes, 1)))
+    if mutate:
+        mutate(args)
+    return L.boost_lrblock_bwd(ctypes.byref(desc), args["x"], args["g"], args["A"], args["B"], args["H"],
+                               args["s"], args["dY"], args["dx"], args["dg"], args["dA"], args["dB"], args["ws"],
+                               ws_bytes, None)
+
+
+def desc_(B, **kw):
+    base = dict(T=300, d=256, r=64, G=3, d_out=192, dtype=B.DT_BF16, act="silu", norm=True, eps=1e-5)
+    base.update(kw)
+    return B.lrblock_desc(**base)
+
+
+@pytest.mark.parametrize("fwd", [True, False])
+def test_lrblock_validation_errors(B, fwd):
+    E_INV, E_UNS, E_MIS, E_ALI, E_WS, E_VER = 1, 2, 3, 4, 5, 6
+    L = B.lib()
+    dsc = desc_(B)
+    dsc.abi_version = 2
+    assert lrblock_call(B, dsc, fwd) == E_VER
+    assert b"abi_version" in L.boost_last_error_detail()
+    assert lrblock_call(B, desc_(B, d=100), fwd) == E_UNS           # not a multiple of 64
+    assert lrblock_call(B, desc_(B, r=0), fwd) == E_INV
+    assert lrblock_call(B, desc_(B, G=17), fwd) == E_INV
+    assert lrblock_call(B, desc_(B, T=0), fwd) == E_INV
+    assert lrblock_call(B, desc_(B, eps=-1.0), fwd) == E_INV
+    assert lrblock_call(B, desc_(B, eps=float("nan")), fwd) == E_INV
+    assert lrblock_call(B, desc_(B, d_norm=128), fwd) == E_INV      # d_norm < d
+    dsc = desc_(B)
+    dsc.dtype = 7
+    assert lrblock_call(B, dsc, fwd) == E_INV
+    dsc = desc_(B)
+    dsc.act = 5
+    assert lrblock_call(B, dsc, fwd) == E_INV
+    dsc = desc_(B)
+    dsc.norm = 2
+    assert lrblock_call(B, dsc, fwd) == E_INV
+    # pointers
+    assert lrblock_call(B, desc_(B), fwd, mutate=lambda a: a.update(x=None)) == E_INV
+    assert b"x is NULL" in L.boost_last_error_detail()
+    assert lrblock_call(B, desc_(B), fwd, mutate=lambda a: a.update(g=None)) == E_INV
+    assert lrblock_call(B, desc_(B), fwd, mutate=lambda a: a.update(A=a["A"] + 2)) == E_MIS
+    # aliasing: an output on top of an input
+    if fwd:
+        assert lrblock_call(B, desc_(B), fwd, mutate=lambda a: a.update(Y=a["x"])) == E_ALI
+    else:
+        assert lrblock_call(B, desc_(B), fwd, mutate=lambda a: a.update(dx=a["x"])) == E_ALI
+        assert lrblock_call(B, desc_(B), fwd, mutate=lambda a: a.update(ws=a["dB"])) == E_ALI
+    # workspace
+    need = B.lrblock_workspace_size(desc_(B), not fwd)
+    assert need > 0
+    assert lrblock_call(B, desc_(B), fwd, ws_bytes=need - 256) == E_WS
+    assert lrblock_call(B, desc_(B), fwd, mutate=lambda a: a.update(ws=None)) == E_WS
+    # a too-large tensor is refused (buffer addressing is 32-bit)
+    assert lrblock_call(B, desc_(B, T=1 << 20, d=2048), fwd) == E_UNS
+
+
+def test_norm0_accepts_null_gain_and_stats(B):
+    # norm = 0 (an O-projection): g, sumsq and dg may be NULL. With every
+    # other argument valid, only the workspace check is left to fail.
+    need = B.lrblock_workspace_size(desc_(B, norm=False), True)
+    r = lrblock_call(B, desc_(B, norm=False), False, ws_bytes=need - 256,
+                     mutate=lambda a: a.update(g=None, s=None, dg=None))
+    assert r == 5
+    r = lrblock_call(B, desc_(B, norm=False), True, ws_bytes=1,
+                     mutate=lambda a: a.update(g=None, s=None))
+    assert r == 5
+
+
+def test_mlp_and_btp_validation(B):
+    L = B.lib()
+    d = B.lrmlp_desc(128, 256, 64, 100, B.DT_BF16)
+    n = ctypes.c_size_t(0)
+    assert L.boost_lrmlp_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == 2   # ffn % 64
+    d = B.lrmlp_desc(128, 256, 64, 192, B.DT_BF16)
+    d.reserved = 1
+    assert L.boost_lrmlp_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == 1
+    d = B.lrmlp_desc(128, 256, 64, 192, B.DT_BF16)
+    assert L.boost_lrmlp_workspace_size(ctypes.byref(d), 1, None) == 1
+    f = Fake()
+    args = [f(1 << 20) for _ in range(10)]
+    assert L.boost_lrmlp_fwd(ctypes.byref(d), *args, None, 0, None) == 5
+    args[0] = None
+    assert L.boost_lrmlp_fwd(ctypes.byref(d), *args, None, 0, None) == 1
+    b = B.btp_desc(128, 64, 96, B.DT_BF16)
+    assert L.boost_btp_share_workspace_size(ctypes.byref(b), 0, ctypes.byref(n)) == 2
+    b = B.btp_desc(128, 64, 128, B.DT_F32)
+    assert L.boost_btp_share_workspace_size(ctypes.byref(b), 1, ctypes.byref(n)) == 0
+    assert n.value > 0
+
+
+def test_workspace_sizes_scale_with_tokens(B):
+    small = B.lrmlp_workspace_size(B.lrmlp_desc(256, 4096, 1024, 11008, B.DT_BF16), True)
+    big = B.lrmlp_workspace_size(B.lrmlp_desc(8192, 4096, 1024, 11008, B.DT_BF16), True)
+    assert 16 < big / small < 40
