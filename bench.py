@@ -311,6 +311,9 @@ def main():
     ap.add_argument("--act", default=None, help="bottleneck activation for the layer set (silu|identity)")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before timing, copy this many MiB once with a plain device copy, so that a "
+                         "counter profile of this run holds a copy kernel of known traffic")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -330,6 +333,16 @@ def main():
     if args.act and wl.kind == "layerset":
         wl.act = args.act
     log(f"workload {args.workload} {wl.shape}; step flops {wl.flops / 1e9:.1f} GF")
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
 
     for _ in range(args.warmup):
         wl.step()

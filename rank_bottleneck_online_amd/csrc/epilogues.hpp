@@ -26,28 +26,64 @@ __device__ __forceinline__ float rms_scale(float sumsq, float inv_dnorm, float e
   return 1.f / sqrtf(sumsq * inv_dnorm + eps);
 }
 
-template <class C>
-using AccT = floatx16[C::NACC][C::FM][C::FN];
+// ---------------------------------------------------------------------------
+// 8-wide vector access to global tensors (16 bytes of bf16, 32 of fp32).
+// Every column offset handed to an epilogue is a multiple of 8 and every
+// row length is a multiple of 64, so these are always aligned.
+// ---------------------------------------------------------------------------
+template <typename T> struct Vec8;
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const void* base, int64_t i, float (&o)[8]) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+    const float4 a = p[0], b = p[1];
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(void* base, int64_t i, const float (&v)[8]) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + i);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+template <> struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const void* base, int64_t i, float (&o)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + i);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = __uint_as_float(ws[q] << 16);
+      o[2 * q + 1] = __uint_as_float(ws[q] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(void* base, int64_t i, const float (&v)[8]) {
+    uint32_t ws[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x2 h;
+      h[0] = static_cast<bf16>(v[2 * q]);      // round to nearest even
+      h[1] = static_cast<bf16>(v[2 * q + 1]);
+      ws[q] = __builtin_bit_cast(uint32_t, h);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + i) = u32x4{ws[0], ws[1], ws[2], ws[3]};
+  }
+};
 
-// Visit the rows of this lane's accumulators: f(i, v, local_row) with
-// compile-time i (row block) and v (element). Accumulator columns are then
-// visited with for_cols; indices stay compile-time throughout.
-template <class C, class F>
-__device__ __forceinline__ void for_rows(const TileCtx& c, F&& f) {
-  static_for<0, C::FM>([&](auto i) { static_for<0, 16>([&](auto v) { f(i, v, acc_row<C>(c, i, v)); }); });
-}
-template <class C, class F>
-__device__ __forceinline__ void for_cols(const TileCtx& c, F&& f) {
-  static_for<0, C::FN>([&](auto j) { f(j, acc_col<C>(c, j)); });
-}
+// Defaults for functors that need no preparation or reductions.
+struct EpiBase {
+  static constexpr bool kRowSumsq = false, kRowSum = false, kColSum = false;
+  template <class C, class A>
+  static __device__ __forceinline__ void begin(const TileCtx&, const A&) {}
+  template <class C, class A>
+  static __device__ __forceinline__ void rows_done(const TileCtx&, const A&, const float*) {}
+  template <class C, class A>
+  static __device__ __forceinline__ void cols_done(const TileCtx&, const A&, const float*) {}
+};
 
 // ---------------------------------------------------------------------------
 // out = acc (optionally row-scaled), dtype or fp32. Also the split-K partial
 // writer (out then points at the partial buffer, indexed by prob).
 // ---------------------------------------------------------------------------
 template <bool F32>
-struct EpiStore {
-  static constexpr bool kRowSumsq = false;
+struct EpiStore : EpiBase {
   struct Args {
     void* out;
     int64_t ldo;
@@ -55,19 +91,24 @@ struct EpiStore {
     const void* rowscale;     // dtype [M] or null
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
+  static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
+    typedef typename C::T T;
+    if (a.rowscale)
+      for (int r = c.t; r < C::BM; r += C::NT)
+        c.rowv[r] = c.m0 + r < c.M ? Elem<T>::load(a.rowscale, c.m0 + r) : 0.f;
+  }
+  template <class C>
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
     typedef typename C::T T;
     typedef typename std::conditional<F32, float, T>::type O;
-    const int64_t base = (int64_t)c.prob * a.pstride;
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      const float rs = a.rowscale ? Elem<T>::load(a.rowscale, row) : 1.f;
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col < c.N) Elem<O>::store(a.out, base + (int64_t)row * a.ldo + col, rs * acc[0][i][j][v()]);
-      });
-    });
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    const float rs = a.rowscale ? c.rowv[lr] : 1.f;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = rs * v[0][e];
+    Vec8<O>::store(a.out, (int64_t)c.prob * a.pstride + (int64_t)row * a.ldo + col, o);
   }
 };
 
@@ -77,7 +118,7 @@ struct EpiStore {
 // products), sumsq from the A loader's row statistics (tile column 0 writes).
 // ---------------------------------------------------------------------------
 template <bool NORM>
-struct EpiDown {
+struct EpiDown : EpiBase {
   static constexpr bool kRowSumsq = NORM;
   struct Args {
     float* H;
@@ -88,51 +129,54 @@ struct EpiDown {
     int act;
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
-    typedef typename C::T T;
+  static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
     if constexpr (NORM) {
-      if (c.tn == 0 && c.split == 0)
-        for (int r = c.t; r < C::BM; r += C::NT)
-          if (c.m0 + r < c.M) a.sumsq[c.m0 + r] = c.rowv[r];
+      // rowv holds the row sums of squares; publish them and turn them into rho.
+      for (int r = c.t; r < C::BM; r += C::NT) {
+        const float ss = c.rowv[r];
+        if (c.tn == 0 && c.split == 0 && c.m0 + r < c.M) a.sumsq[c.m0 + r] = ss;
+        c.rowv[r] = rms_scale(ss, a.inv_dnorm, a.eps);
+      }
     }
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      const float rho = NORM ? rms_scale(c.rowv[lr], a.inv_dnorm, a.eps) : 1.f;
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col >= c.N) return;
-        const float h = rho * acc[0][i][j][v()];
-        const int64_t o = (int64_t)row * a.ld + col;
-        a.H[o] = h;
-        Elem<T>::store(a.S, o, act_f(h, a.act));
-      });
-    });
+  }
+  template <class C>
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
+    typedef typename C::T T;
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    const float rho = NORM ? c.rowv[lr] : 1.f;
+    float h[8], sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[e] = rho * v[0][e];
+      sv[e] = act_f(h[e], a.act);
+    }
+    const int64_t o = (int64_t)row * a.ld + col;
+    Vec8<float>::store(a.H, o, h);
+    Vec8<T>::store(a.S, o, sv);
   }
 };
 
 // ---------------------------------------------------------------------------
 // SwiGLU on two accumulators of the same tile: M = SiLU(gate) * up.
 // ---------------------------------------------------------------------------
-struct EpiSwiglu {
-  static constexpr bool kRowSumsq = false;
+struct EpiSwiglu : EpiBase {
   struct Args {
     void* M;
     int64_t ld;
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
     typedef typename C::T T;
     static_assert(C::NACC == 2, "SwiGLU needs two accumulators");
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col < c.N)
-          Elem<T>::store(a.M, (int64_t)row * a.ld + col, silu_f(acc[0][i][j][v()]) * acc[1][i][j][v()]);
-      });
-    });
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = silu_f(v[0][e]) * v[1][e];
+    Vec8<T>::store(a.M, (int64_t)row * a.ld + col, m);
   }
 };
 
@@ -143,49 +187,54 @@ struct EpiSwiglu {
 // (the rho-gradient, dRho = q / rho), one row of partials per (j, tile col).
 // ---------------------------------------------------------------------------
 template <bool NORM>
-struct EpiDS {
-  static constexpr bool kRowSumsq = false;
+struct EpiDS : EpiBase {
+  static constexpr bool kRowSum = NORM;
   struct Args {
     const float* H;
     int64_t ld;        // columns of H, dU, S (= G*r)
     int64_t r;         // group width (column offset of group j is j*r)
     void* dU;
     void* S;           // may be null
-    float* qpart;      // [G*tiles_n][qstride] or null
+    float* qpart;      // [G*tiles_n][qstride] (NORM only)
     int64_t qstride;
     const float* sumsq;
     float inv_dnorm, eps;
     int act;
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
-    typedef typename C::T T;
-    const int64_t goff = (int64_t)c.bidx * a.r;
-    float part[C::FM][16];
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      part[i][v] = 0.f;
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      const float rho = NORM ? rms_scale(a.sumsq[row], a.inv_dnorm, a.eps) : 1.f;
-      float q = 0.f;
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col >= c.N) return;
-        const int64_t o = (int64_t)row * a.ld + goff + col;
-        const float h = a.H[o];
-        const float dh = acc[0][i][j][v()] * act_grad_f(h, a.act);
-        Elem<T>::store(a.dU, o, rho * dh);
-        if (a.S) Elem<T>::store(a.S, o, act_f(h, a.act));
-        q += dh * h;
-      });
-      part[i][v] = q;
-    });
-    if (a.qpart) {
-      tile_row_sum<C>(c, part, c.rowv);
-      const int64_t slot = (int64_t)c.bidx * cdiv(c.N, C::BN) + c.tn;
-      float* qp = a.qpart + slot * a.qstride;
+  static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
+    if constexpr (NORM)
       for (int r = c.t; r < C::BM; r += C::NT)
-        if (c.m0 + r < c.M) qp[c.m0 + r] = c.rowv[r];
+        c.rowv[r] = c.m0 + r < c.M ? rms_scale(a.sumsq[c.m0 + r], a.inv_dnorm, a.eps) : 0.f;
+  }
+  template <class C>
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float& rowc, float (&)[8]) {
+    typedef typename C::T T;
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    const int64_t o = (int64_t)row * a.ld + (int64_t)c.bidx * a.r + col;
+    const float rho = NORM ? c.rowv[lr] : 1.f;
+    float h[8], du[8], sv[8];
+    Vec8<float>::load(a.H, o, h);
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float dh = v[0][e] * act_grad_f(h[e], a.act);
+      du[e] = rho * dh;
+      sv[e] = act_f(h[e], a.act);
+      q += dh * h[e];
+    }
+    Vec8<T>::store(a.dU, o, du);
+    if (a.S) Vec8<T>::store(a.S, o, sv);
+    rowc = q;
+  }
+  template <class C>
+  static __device__ __forceinline__ void rows_done(const TileCtx& c, const Args& a, const float* sums) {
+    if constexpr (NORM) {
+      float* qp = a.qpart + ((int64_t)c.bidx * cdiv(c.N, C::BN) + c.tn) * a.qstride;
+      for (int r = c.t; r < C::BM; r += C::NT)
+        if (c.m0 + r < c.M) qp[c.m0 + r] = sums[r];
     }
   }
 };
@@ -195,8 +244,8 @@ struct EpiDS {
 // dx = g * dx~ - (rho^2 q / d_norm) * x   (rho^3 dRho / d_norm, dRho = q/rho)
 // and per-column partials of dg = sum_t x * dx~ over this tile's rows.
 // ---------------------------------------------------------------------------
-struct EpiDX {
-  static constexpr bool kRowSumsq = false;
+struct EpiDX : EpiBase {
+  static constexpr bool kColSum = true;
   struct Args {
     const void* x;
     const void* g;
@@ -210,8 +259,7 @@ struct EpiDX {
     int64_t ld;     // d
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
-    typedef typename C::T T;
+  static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
     for (int r = c.t; r < C::BM; r += C::NT) {
       const int row = c.m0 + r;
       float coef = 0.f;
@@ -223,30 +271,29 @@ struct EpiDX {
       }
       c.rowv[r] = coef;
     }
-    __syncthreads();
-    float part[C::FN], gv[C::FN];
-    for_cols<C>(c, [&](auto j, int lc) {
-      const int col = c.n0 + lc;
-      gv[j] = col < c.N ? Elem<T>::load(a.g, col) : 0.f;
-      part[j] = 0.f;
-    });
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      const float coef = c.rowv[lr];
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col >= c.N) return;
-        const int64_t o = (int64_t)row * a.ld + col;
-        const float xv = Elem<T>::load(a.x, o);
-        const float d = acc[0][i][j][v()];
-        Elem<T>::store(a.dx, o, gv[j] * d - coef * xv);
-        part[j] += xv * d;
-      });
-    });
-    tile_col_sum<C>(c, part, c.colv);
+  }
+  template <class C>
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float&, float (&colc)[8]) {
+    typedef typename C::T T;
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    const int64_t o = (int64_t)row * a.ld + col;
+    const float coef = c.rowv[lr];
+    float xv[8], gv[8], dx[8];
+    Vec8<T>::load(a.x, o, xv);
+    Vec8<T>::load(a.g, col, gv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dx[e] = gv[e] * v[0][e] - coef * xv[e];
+      colc[e] += xv[e] * v[0][e];
+    }
+    Vec8<T>::store(a.dx, o, dx);
+  }
+  template <class C>
+  static __device__ __forceinline__ void cols_done(const TileCtx& c, const Args& a, const float* sums) {
     for (int n = c.t; n < C::BN; n += C::NT)
-      if (c.n0 + n < c.N) a.dgpart[(int64_t)c.tm * a.ld + c.n0 + n] = c.colv[n];
+      if (c.n0 + n < c.N) a.dgpart[(int64_t)c.tm * a.ld + c.n0 + n] = sums[n];
   }
 };
 
@@ -255,8 +302,7 @@ struct EpiDX {
 // Reads dM (fp32); writes M = SiLU(Yg) Yu (operand of dA2), and
 // dYg = dM Yu SiLU'(Yg), dYu = dM SiLU(Yg) into a [2,T,ffn] buffer.
 // ---------------------------------------------------------------------------
-struct EpiSwigluBwd {
-  static constexpr bool kRowSumsq = false;
+struct EpiSwigluBwd : EpiBase {
   struct Args {
     const float* dM;
     void* M;
@@ -265,25 +311,27 @@ struct EpiSwigluBwd {
     int64_t ystride; // T * ffn
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
     typedef typename C::T T;
     static_assert(C::NACC == 2, "SwiGLU backward needs two accumulators");
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col >= c.N) return;
-        const int64_t o = (int64_t)row * a.ld + col;
-        const float yg = acc[0][i][j][v()], yu = acc[1][i][j][v()];
-        const float dm = a.dM[o];
-        const float s = sigmoid_f(yg);
-        const float sl = yg * s;
-        Elem<T>::store(a.M, o, sl * yu);
-        Elem<T>::store(a.dYgu, o, dm * yu * (s * (1.f + yg * (1.f - s))));
-        Elem<T>::store(a.dYgu, a.ystride + o, dm * sl);
-      });
-    });
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    const int64_t o = (int64_t)row * a.ld + col;
+    float dm[8], m[8], dg[8], du[8];
+    Vec8<float>::load(a.dM, o, dm);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float yg = v[0][e], yu = v[1][e];
+      const float s = sigmoid_f(yg);
+      const float sl = yg * s;
+      m[e] = sl * yu;
+      dg[e] = dm[e] * yu * (s * (1.f + yg * (1.f - s)));
+      du[e] = dm[e] * sl;
+    }
+    Vec8<T>::store(a.M, o, m);
+    Vec8<T>::store(a.dYgu, o, dg);
+    Vec8<T>::store(a.dYgu, a.ystride + o, du);
   }
 };
 
@@ -292,8 +340,8 @@ struct EpiSwigluBwd {
 // a = SiLU(u); writes (a * g_s) (dtype, operand of the row-slice product) and
 // per-row partial sums of a^2 over this tile's columns.
 // ---------------------------------------------------------------------------
-struct EpiBtpU {
-  static constexpr bool kRowSumsq = false;
+struct EpiBtpU : EpiBase {
+  static constexpr bool kRowSum = true;
   struct Args {
     const void* g;
     void* ag;
@@ -302,31 +350,27 @@ struct EpiBtpU {
     int64_t ld;    // d_shard
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float& rowc, float (&)[8]) {
     typedef typename C::T T;
-    float gv[C::FN];
-    for_cols<C>(c, [&](auto j, int lc) {
-      const int col = c.n0 + lc;
-      gv[j] = col < c.N ? Elem<T>::load(a.g, col) : 0.f;
-    });
-    float part[C::FM][16];
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      part[i][v] = 0.f;
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      float s = 0.f;
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col >= c.N) return;
-        const float av = silu_f(acc[0][i][j][v()]);
-        Elem<T>::store(a.ag, (int64_t)row * a.ld + col, av * gv[j]);
-        s += av * av;
-      });
-      part[i][v] = s;
-    });
-    tile_row_sum<C>(c, part, c.rowv);
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    float gv[8], ag[8];
+    Vec8<T>::load(a.g, col, gv);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float av = silu_f(v[0][e]);
+      ag[e] = av * gv[e];
+      s += av * av;
+    }
+    Vec8<T>::store(a.ag, (int64_t)row * a.ld + col, ag);
+    rowc = s;
+  }
+  template <class C>
+  static __device__ __forceinline__ void rows_done(const TileCtx& c, const Args& a, const float* sums) {
     for (int r = c.t; r < C::BM; r += C::NT)
-      if (c.m0 + r < c.M) a.spart[(int64_t)c.tn * a.sstride + c.m0 + r] = c.rowv[r];
+      if (c.m0 + r < c.M) a.spart[(int64_t)c.tn * a.sstride + c.m0 + r] = sums[r];
   }
 };
 
@@ -334,8 +378,7 @@ struct EpiBtpU {
 // Tensor-parallel share, forward, second product: acc = p (partial over
 // shares). Tile column 0 also sums the row partials of a^2 into s.
 // ---------------------------------------------------------------------------
-struct EpiBtpP {
-  static constexpr bool kRowSumsq = false;
+struct EpiBtpP : EpiBase {
   struct Args {
     void* p;
     int64_t ld;  // r
@@ -345,8 +388,7 @@ struct EpiBtpP {
     float* s;
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
-    typedef typename C::T T;
+  static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
     if (c.tn == 0) {
       for (int r = c.t; r < C::BM; r += C::NT) {
         const int row = c.m0 + r;
@@ -356,14 +398,17 @@ struct EpiBtpP {
         a.s[row] = s;
       }
     }
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col < c.N) Elem<T>::store(a.p, (int64_t)row * a.ld + col, acc[0][i][j][v()]);
-      });
-    });
+  }
+  template <class C>
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
+    typedef typename C::T T;
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = v[0][e];
+    Vec8<T>::store(a.p, (int64_t)row * a.ld + col, o);
   }
 };
 
@@ -374,8 +419,8 @@ struct EpiBtpP {
 // writes du (dtype), a * g_s (dtype, operand of dA_s) and per-column
 // partials of dg_s = sum_t a e over this tile's rows.
 // ---------------------------------------------------------------------------
-struct EpiBtpUBwd {
-  static constexpr bool kRowSumsq = false;
+struct EpiBtpUBwd : EpiBase {
+  static constexpr bool kColSum = true;
   struct Args {
     const float* e;
     const float* ds;
@@ -386,35 +431,37 @@ struct EpiBtpUBwd {
     int64_t ld;     // d_shard
   };
   template <class C>
-  static __device__ __forceinline__ void run(AccT<C>& acc, const TileCtx& c, const Args& a) {
+  static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
+    for (int r = c.t; r < C::BM; r += C::NT) c.rowv[r] = c.m0 + r < c.M ? a.ds[c.m0 + r] : 0.f;
+  }
+  template <class C>
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], float&, float (&colc)[8]) {
     typedef typename C::T T;
-    float gv[C::FN], part[C::FN];
-    for_cols<C>(c, [&](auto j, int lc) {
-      const int col = c.n0 + lc;
-      gv[j] = col < c.N ? Elem<T>::load(a.g, col) : 0.f;
-      part[j] = 0.f;
-    });
-    for_rows<C>(c, [&](auto i, auto v, int lr) {
-      const int row = c.m0 + lr;
-      if (row >= c.M) return;
-      const float dsv = a.ds[row];
-      for_cols<C>(c, [&](auto j, int lc) {
-        const int col = c.n0 + lc;
-        if (col >= c.N) return;
-        const int64_t o = (int64_t)row * a.ld + col;
-        const float u = acc[0][i][j][v()];
-        const float s = sigmoid_f(u);
-        const float av = u * s;
-        const float ev = a.e[o];
-        const float da = gv[j] * ev + 2.f * dsv * av;
-        Elem<T>::store(a.du, o, da * (s * (1.f + u * (1.f - s))));
-        Elem<T>::store(a.ag, o, av * gv[j]);
-        part[j] += av * ev;
-      });
-    });
-    tile_col_sum<C>(c, part, c.colv);
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    const int64_t o = (int64_t)row * a.ld + col;
+    const float dsv = c.rowv[lr];
+    float ev[8], gv[8], du[8], ag[8];
+    Vec8<float>::load(a.e, o, ev);
+    Vec8<T>::load(a.g, col, gv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float u = v[0][e];
+      const float s = sigmoid_f(u);
+      const float av = u * s;
+      const float da = gv[e] * ev[e] + 2.f * dsv * av;
+      du[e] = da * (s * (1.f + u * (1.f - s)));
+      ag[e] = av * gv[e];
+      colc[e] += av * ev[e];
+    }
+    Vec8<T>::store(a.du, o, du);
+    Vec8<T>::store(a.ag, o, ag);
+  }
+  template <class C>
+  static __device__ __forceinline__ void cols_done(const TileCtx& c, const Args& a, const float* sums) {
     for (int n = c.t; n < C::BN; n += C::NT)
-      if (c.n0 + n < c.N) a.dgpart[(int64_t)c.tm * a.ld + c.n0 + n] = c.colv[n];
+      if (c.n0 + n < c.N) a.dgpart[(int64_t)c.tm * a.ld + c.n0 + n] = sums[n];
   }
 };
 

@@ -28,9 +28,15 @@
 // K tail of K = tokens products need no branches. Reads past M or N inside
 // the tensor only feed accumulator rows/columns that the epilogue masks.
 //
-// Pipelining: two LDS stages; the next K slab is fetched into registers while
-// the MFMAs consume the current stage, then written to the other stage; one
-// barrier per K step.
+// Pipelining: two LDS stages and one set of staging registers. During K step
+// kt the MFMAs read stage kt%2 while the slab of step kt+1 (already in the
+// staging registers since the previous step) is written to the other stage
+// and the slab of step kt+2 is fetched from HBM, so each global load has a
+// whole K step to land. MFMA fragments are double-buffered across the
+// 16-wide k sub-steps. The loop body has no branches (the slabs past the end
+// of K are read through the buffer range check and never consumed), which
+// lets the scheduler interleave LDS, global and MFMA work; one barrier per
+// K step.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -136,9 +142,17 @@ struct Cfg {
   static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int PIPE_BYTES = 2 * STAGE_BYTES;
-  // After the pipeline: per-row and per-column fp32 vectors for epilogues.
-  static constexpr int VEC_BYTES = (BM + BN) * 4;
-  static constexpr int LDS_BYTES = PIPE_BYTES + VEC_BYTES;
+  // Epilogue staging: each wave writes 32 accumulator rows at a time (per
+  // accumulator) into a private fp32 buffer with a row stride padded by 8
+  // floats (the two half-waves of the MFMA layout then hit disjoint banks),
+  // reusing the pipeline LDS.
+  static constexpr int EPI_STR = WTN + 8;
+  static constexpr int EPI_SUB = 32 * EPI_STR;
+  static constexpr int EPI_BYTES = WM * WN * NACC * EPI_SUB * 4;
+  static constexpr int SCR_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
+  // After that: per-row / per-column fp32 vectors and reduction partials.
+  static constexpr int VEC_BYTES = (BM + BN + WN * BM + WM * BN) * 4;
+  static constexpr int LDS_BYTES = SCR_BYTES + VEC_BYTES;
   static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA block");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
 };
@@ -172,10 +186,12 @@ struct TileCtx {
   int bidx, split;   // batch index, K-split index
   int prob;          // bidx * splits + split
   int M, N;
-  int t, lane, wm, wn;
+  int t, lane, wave, wm, wn;
   char* smem;        // pipeline LDS, free for epilogue scratch
   float* rowv;       // BM fp32 in LDS (row statistics from the A loader)
   float* colv;       // BN fp32 in LDS
+  float* rowpart;    // [WN][BM] fp32 in LDS (row-sum partials per wave column)
+  float* colpart;    // [WM][BN] fp32 in LDS (column-sum partials per wave row)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -242,14 +258,20 @@ struct Loader {
   }
 
   // Write the fetched slab into an LDS tile (K-contiguous rows).
-  __device__ __forceinline__ void store(char* tile, int t) {
+  // `count` says whether this slab lies inside the K range (the pipeline
+  // runs one slab past the end; that slab is never read, and its values must
+  // not enter the row statistics).
+  __device__ __forceinline__ void store(char* tile, int t, bool count = true) {
     if constexpr (KC) {
       const int c = t & 7;
 #pragma unroll
       for (int u = 0; u < KC_UNITS; ++u) {
         const int row = (t >> 3) + u * (C::NT / 8);
         *reinterpret_cast<u32x4*>(tile + lds_off(row, c)) = r[u];
-        if constexpr (ROWSUMSQ) ss[u] = sumsq16(r[u], ss[u]);
+        if constexpr (ROWSUMSQ) {
+          const float add = sumsq16(r[u], 0.f);
+          ss[u] += count ? add : 0.f;
+        }
       }
     } else {
       const int tt = FROM_TOP ? (C::NT - 1 - t) : t;
@@ -334,6 +356,112 @@ __device__ __forceinline__ void group_tile(int tile, int tiles_m, int tiles_n, i
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue driver.
+//
+// The accumulators are handed to the epilogue through LDS, 32 rows of each
+// wave's tile at a time: the wave writes them in the MFMA layout into its
+// private padded buffer, then reads them back row-contiguously, 8 columns
+// per lane (a row of the wave tile is WTN/8 consecutive lanes). The
+// epilogue functor E sees (tile row, tile column, 8 values per accumulator)
+// and does all of its global traffic as 16-byte vectors. E may return a
+// per-row contribution (summed over the tile's columns) and 8 per-column
+// contributions (summed over the tile's rows); both sums are formed here in
+// a fixed order (lane butterflies, then waves in index order), so results
+// are bit-reproducible.
+//
+// Functor interface:
+//   kRowSumsq           the A loader accumulates row sums of squares into rowv
+//   kRowSum / kColSum   the reductions above are wanted
+//   begin(c, a)         per-tile preparation (all threads; a barrier follows)
+//   apply(c, a, lr, lc, v, rowc, colc)   lr/lc tile-local row / first column
+//   rows_done(c, a, sums) / cols_done(c, a, sums)   sums in LDS, BM / BN long
+// ---------------------------------------------------------------------------
+template <class C, class E>
+__device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN], const TileCtx& c,
+                                         const typename E::Args& ea) {
+  constexpr int STR = C::EPI_STR, SUB = C::EPI_SUB;
+  constexpr int V8 = C::WTN / 8;        // lanes per row in the read-back
+  constexpr int RPS = 64 / V8;          // rows per read-back step
+  constexpr int STEPS = 32 / RPS;
+  static_assert(64 % V8 == 0 && 32 % RPS == 0, "wave tile width must be 32, 64 or 128");
+  float* scr = reinterpret_cast<float*>(c.smem) + c.wave * (C::NACC * SUB);
+  const int c8 = c.lane % V8, rsub = c.lane / V8;
+
+  E::template begin<C>(c, ea);
+  __syncthreads();
+
+  float colc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) colc[e] = 0.f;
+
+  static_for<0, C::FM>([&](auto i) {
+    static_for<0, C::NACC>([&](auto p) {
+      static_for<0, C::FN>([&](auto j) {
+        static_for<0, 16>([&](auto v) {
+          constexpr int r0 = (v >> 2) * 8 + (v & 3);
+          scr[p * SUB + (r0 + (c.lane >> 5) * 4) * STR + j * 32 + (c.lane & 31)] = acc[p][i][j][v()];
+        });
+      });
+    });
+    __syncthreads();
+    for (int s = 0; s < STEPS; ++s) {
+      const int r = s * RPS + rsub;
+      const int lr = c.wm * C::WTM + i * 32 + r;
+      const int lc = c.wn * C::WTN + c8 * 8;
+      float vals[C::NACC][8];
+      static_for<0, C::NACC>([&](auto p) {
+        const float* src = scr + p * SUB + r * STR + c8 * 8;
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
+        vals[p][0] = a.x; vals[p][1] = a.y; vals[p][2] = a.z; vals[p][3] = a.w;
+        vals[p][4] = b.x; vals[p][5] = b.y; vals[p][6] = b.z; vals[p][7] = b.w;
+      });
+      float rowc = 0.f;
+      E::template apply<C>(c, ea, lr, lc, vals, rowc, colc);
+      if constexpr (E::kRowSum) {
+#pragma unroll
+        for (int m = 1; m < V8; m <<= 1) rowc += __shfl_xor(rowc, m);
+        if (c8 == 0) c.rowpart[c.wn * C::BM + lr] = rowc;
+      }
+    }
+    __syncthreads();
+  });
+
+  if constexpr (E::kColSum) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int m = V8; m < 64; m <<= 1) colc[e] += __shfl_xor(colc[e], m);
+    if (c.lane < V8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c.colpart[c.wm * C::BN + c.wn * C::WTN + c.lane * 8 + e] = colc[e];
+    }
+  }
+  if constexpr (E::kRowSum || E::kColSum) {
+    __syncthreads();
+    if constexpr (E::kRowSum) {
+      for (int r = c.t; r < C::BM; r += C::NT) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::WN; ++w) s += c.rowpart[w * C::BM + r];
+        c.rowv[r] = s;
+      }
+    }
+    if constexpr (E::kColSum) {
+      for (int n = c.t; n < C::BN; n += C::NT) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::WM; ++w) s += c.colpart[w * C::BN + n];
+        c.colv[n] = s;
+      }
+    }
+    __syncthreads();
+    if constexpr (E::kRowSum) E::template rows_done<C>(c, ea, c.rowv);
+    if constexpr (E::kColSum) E::template cols_done<C>(c, ea, c.colv);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
 template <class C, class E>
@@ -373,8 +501,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
   Loader<C, C::BN, C::BKC, true, false> lb;
   la.init();
 
-#pragma unroll
-  for (int p = 0; p < C::NACC; ++p) {
+  static_for<0, C::NACC>([&](auto p) {
     const Operand& A = ops.a[p];
     const Operand& B = ops.b[p];
     // Rebase each operand on this tile so 32-bit buffer offsets suffice.
@@ -392,40 +519,52 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
     lb.fetch(rb, ldb_b, kbeg, t);
     la.store(smem, t);
     lb.store(smem + C::A_BYTES, t);
-    __syncthreads();
+    la.fetch(ra, lda_b, kbeg + C::BK, t);
+    lb.fetch(rb, ldb_b, kbeg + C::BK, t);
 
+    constexpr int KK = C::BK / MF::KI;
     for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < KT;
-      if (more) {
-        la.fetch(ra, lda_b, kbeg + (kt + 1) * C::BK, t);
-        lb.fetch(rb, ldb_b, kbeg + (kt + 1) * C::BK, t);
-      }
-      const char* As = smem + cur * C::STAGE_BYTES;
-      const char* Bs = As + C::A_BYTES;
-#pragma unroll
-      for (int kk = 0; kk < C::BK / MF::KI; ++kk) {
-        const int k = kk * MF::KI + (lane >> 5) * MF::KL;
-        typename MF::Frag fa[C::FM], fb[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) fa[i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), k);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) fb[j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), k);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) acc[p][i][j] = MF::mma(fa[i], fb[j], acc[p][i][j]);
-      }
-      if (more) {
-        char* nx = smem + (cur ^ 1) * C::STAGE_BYTES;
-        la.store(nx, t);
-        lb.store(nx + C::A_BYTES, t);
-      }
       __syncthreads();
+      const char* As = smem + (kt & 1) * C::STAGE_BYTES;
+      const char* Bs = As + C::A_BYTES;
+      char* Ns = smem + ((kt & 1) ^ 1) * C::STAGE_BYTES;
+      const bool next_in_k = kt + 1 < KT;
+      typename MF::Frag fa[2][C::FM], fb[2][C::FN];
+      const int kl = (lane >> 5) * MF::KL;
+      static_for<0, C::FM>([&](auto i) { fa[0][i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), kl); });
+      static_for<0, C::FN>([&](auto j) { fb[0][j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), kl); });
+      static_for<0, KK>([&](auto kk) {
+        constexpr int cur = kk & 1, nxt = cur ^ 1;
+        if constexpr (kk + 1 < KK) {
+          const int k = (kk + 1) * MF::KI + kl;
+          static_for<0, C::FM>([&](auto i) { fa[nxt][i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), k); });
+          static_for<0, C::FN>([&](auto j) { fb[nxt][j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), k); });
+        }
+        static_for<0, C::FM>([&](auto i) {
+          static_for<0, C::FN>([&](auto j) { acc[p][i][j] = MF::mma(fa[cur][i], fb[cur][j], acc[p][i][j]); });
+        });
+        // Staging work after the first two sub-steps' MFMAs have been issued:
+        // each operand's slab for step kt+1 goes to the other LDS stage and
+        // its registers are refilled at once with step kt+2, so every global
+        // load has a whole K step to land. The scheduling barriers keep the
+        // compiler from sinking the loads to the end of the step.
+        if constexpr (kk == 0 || kk == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kk == 0) {
+            la.store(Ns, t, next_in_k);
+            la.fetch(ra, lda_b, kbeg + (kt + 2) * C::BK, t);
+          } else {
+            lb.store(Ns + C::A_BYTES, t);
+            lb.fetch(rb, ldb_b, kbeg + (kt + 2) * C::BK, t);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
     }
-  }
+    __syncthreads();
+  });
 
-  float* rowv = reinterpret_cast<float*>(smem + C::PIPE_BYTES);
+  float* rowv = reinterpret_cast<float*>(smem + C::SCR_BYTES);
   float* colv = rowv + C::BM;
   if constexpr (RSS) {
     // Row sums of squares of A (the Online-RMSNorm statistic): the 8 lanes
@@ -443,68 +582,11 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
 
   TileCtx c;
   c.m0 = m0; c.n0 = n0; c.tm = tm; c.tn = tn; c.bidx = bidx; c.split = split; c.prob = prob;
-  c.M = g.M; c.N = g.N; c.t = t; c.lane = lane; c.wm = wm; c.wn = wn;
+  c.M = g.M; c.N = g.N; c.t = t; c.lane = lane; c.wave = wave; c.wm = wm; c.wn = wn;
   c.smem = smem; c.rowv = rowv; c.colv = colv;
-  E::template run<C>(acc, c, ea);
-}
-
-// ---------------------------------------------------------------------------
-// Epilogue helpers over the accumulator layout
-// ---------------------------------------------------------------------------
-template <class C>
-__device__ __forceinline__ int acc_row(const TileCtx& c, int i, int v) {
-  return c.wm * C::WTM + i * 32 + (v >> 2) * 8 + (c.lane >> 5) * 4 + (v & 3);
-}
-template <class C>
-__device__ __forceinline__ int acc_col(const TileCtx& c, int j) {
-  return c.wn * C::WTN + j * 32 + (c.lane & 31);
-}
-
-// part[i][v] holds this lane's partial for tile row acc_row(i, v) summed over
-// its own columns. On return out[r] (LDS, r < BM) holds the sum over all BN
-// columns of the tile, in a fixed order. Uses the pipeline LDS as scratch.
-template <class C>
-__device__ __forceinline__ void tile_row_sum(const TileCtx& c, float (&part)[C::FM][16], float* out) {
-  float* scr = reinterpret_cast<float*>(c.smem);  // [WN][BM]
-  static_for<0, C::FM>([&](auto i) {
-    static_for<0, 16>([&](auto v) {
-      float s = part[i][v];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      s += __shfl_xor(s, 16);
-      if ((c.lane & 31) == 0) scr[c.wn * C::BM + acc_row<C>(c, i, v)] = s;
-    });
-  });
-  __syncthreads();
-  for (int r = c.t; r < C::BM; r += C::NT) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < C::WN; ++w) s += scr[w * C::BM + r];
-    out[r] = s;
-  }
-  __syncthreads();
-}
-
-// part[j] holds this lane's partial for tile column acc_col(j) summed over
-// its own rows. On return out[n] (LDS, n < BN) holds the column sum over all
-// BM rows of the tile, in a fixed order.
-template <class C>
-__device__ __forceinline__ void tile_col_sum(const TileCtx& c, float (&part)[C::FN], float* out) {
-  float* scr = reinterpret_cast<float*>(c.smem);  // [WM][BN]
-  static_for<0, C::FN>([&](auto j) {
-    const float s = part[j] + __shfl_xor(part[j], 32);
-    if (c.lane < 32) scr[c.wm * C::BN + acc_col<C>(c, j)] = s;
-  });
-  __syncthreads();
-  for (int n = c.t; n < C::BN; n += C::NT) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < C::WM; ++w) s += scr[w * C::BN + n];
-    out[n] = s;
-  }
-  __syncthreads();
+  c.rowpart = colv + C::BN;
+  c.colpart = c.rowpart + C::WN * C::BM;
+  epilogue<C, E>(acc, c, ea);
 }
 
 }  // namespace rbo
