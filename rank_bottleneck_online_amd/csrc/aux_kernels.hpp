@@ -1,5 +1,6 @@
-// Small memory-bound kernels around the GEMMs: folding the RMSNorm gain into
-// the down weights, recomputing the bottleneck activation from the saved
+// Small memory-bound kernels around the GEMMs: transposing weights into the
+// K-contiguous operand layout (folding the RMSNorm gain into the down
+// weights on the way), recomputing the bottleneck activation from the saved
 // fp32 H, and the fixed-order reductions of per-tile partials.
 #pragma once
 
@@ -8,42 +9,44 @@
 
 namespace rbo {
 
-// out[k][n] = g[k] * A[k][n], rounded once to the storage dtype. The gain of
-// RMSNorm multiplies the reduction index of the down product, so scaling
-// the weight rows is the same product as scaling the input columns.
+// out[b][c][r] = scale[r] * in[b][r][c], rounded once to the storage dtype
+// (scale may be null). Turns a weight kept in [in, out] layout into the
+// K-contiguous [out, in] operand of the products; with the RMSNorm gain as
+// the scale it also folds the gain into the down weights. 64 x 64 tiles
+// through LDS, 16-byte global accesses on both sides. R, C multiples of 64.
 template <typename T>
-__global__ __launch_bounds__(256) void gain_fold_kernel(const T* __restrict__ A, const T* __restrict__ g,
-                                                        T* __restrict__ out, int64_t rows, int64_t cols) {
-  const int64_t n = rows * cols;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t k = i / cols;
-    Elem<T>::store(out, i, Elem<T>::load(g, k) * Elem<T>::load(A, i));
-  }
-}
-
-// Vectorised bf16 variant: 8 elements per thread per step (cols % 8 == 0).
-__global__ __launch_bounds__(256) void gain_fold_bf16x8_kernel(const u32x4* __restrict__ A,
-                                                               const uint16_t* __restrict__ g,
-                                                               u32x4* __restrict__ out, int64_t rows,
-                                                               int64_t cols) {
-  const int64_t n8 = rows * cols / 8;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t k = (i * 8) / cols;
-    const float gk = Elem<bf16>::to_f32(g[k]);
-    const u32x4 v = A[i];
-    u32x4 o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float lo = gk * __uint_as_float(v[w] << 16);
-      const float hi = gk * __uint_as_float(v[w] & 0xffff0000u);
-      bf16x2 p;
-      p[0] = static_cast<bf16>(lo);
-      p[1] = static_cast<bf16>(hi);
-      o[w] = __builtin_bit_cast(uint32_t, p);
+__global__ __launch_bounds__(256) void transpose_scale_kernel(const T* __restrict__ in, const T* __restrict__ scale,
+                                                              T* __restrict__ out, int R, int C) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float tile[64][65];
+  const int tr = blockIdx.y * 64, tc = blockIdx.x * 64, b = blockIdx.z;
+  const T* src = in + (int64_t)b * R * C;
+  T* dst = out + (int64_t)b * R * C;
+  const int t = threadIdx.x;
+  for (int q = t; q < 64 * 64 / VEC; q += 256) {
+    const int r = q / (64 / VEC), c = (q % (64 / VEC)) * VEC;
+    float v[8];
+    if constexpr (VEC == 8) {
+      Vec8<bf16>::load(src, (int64_t)(tr + r) * C + tc + c, v);
+    } else {
+      const float4 f = *reinterpret_cast<const float4*>(src + (int64_t)(tr + r) * C + tc + c);
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     }
-    out[i] = o;
+    const float sc = scale ? Elem<T>::load(scale, tr + r) : 1.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) tile[r][c + e] = sc * v[e];
+  }
+  __syncthreads();
+  for (int q = t; q < 64 * 64 / VEC; q += 256) {
+    const int c = q / (64 / VEC), r = (q % (64 / VEC)) * VEC;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] = tile[r + e][c];
+    if constexpr (VEC == 8) {
+      Vec8<bf16>::store(dst, (int64_t)(tc + c) * R + tr + r, v);
+    } else {
+      *reinterpret_cast<float4*>(dst + (int64_t)(tc + c) * R + tr + r) = make_float4(v[0], v[1], v[2], v[3]);
+    }
   }
 }
 

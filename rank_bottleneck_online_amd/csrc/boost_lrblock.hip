@@ -192,19 +192,19 @@ int grid_for(int64_t n, int per_thread = 1) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(blocks, 4096));
 }
 
-int launch_gain_fold(int dtype, const void* A, const void* g, void* out, int64_t rows, int64_t cols,
+// out[b][c][r] = scale[r] * in[b][r][c] (scale may be null).
+int launch_transpose(int dtype, const void* in, const void* scale, void* out, int64_t R, int64_t C, int64_t batch,
                      hipStream_t s) {
-  prof_begin("gain_fold", s);
+  const dim3 grid((unsigned)(C / 64), (unsigned)(R / 64), (unsigned)batch);
+  prof_begin("weight_transpose", s);
   if (dtype == BOOST_DT_BF16)
-    hipLaunchKernelGGL(gain_fold_bf16x8_kernel, dim3(grid_for(rows * cols, 8)), dim3(256), 0, s,
-                       static_cast<const u32x4*>(A), static_cast<const uint16_t*>(g),
-                       static_cast<u32x4*>(out), rows, cols);
+    hipLaunchKernelGGL(transpose_scale_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(in),
+                       static_cast<const bf16*>(scale), static_cast<bf16*>(out), (int)R, (int)C);
   else
-    hipLaunchKernelGGL(gain_fold_kernel<float>, dim3(grid_for(rows * cols)), dim3(256), 0, s,
-                       static_cast<const float*>(A), static_cast<const float*>(g), static_cast<float*>(out),
-                       rows, cols);
+    hipLaunchKernelGGL(transpose_scale_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(in),
+                       static_cast<const float*>(scale), static_cast<float*>(out), (int)R, (int)C);
   prof_end(s);
-  return check_launch("gain_fold");
+  return check_launch("weight_transpose");
 }
 
 int launch_act_quant(int dtype, const float* H, void* S, int64_t n, int act, hipStream_t s) {
@@ -366,7 +366,7 @@ int lrblock_check_desc(const boost_lrblock_desc* d) {
 
 struct LrblockPlan {
   Choice down, up, ds, dB, dA, dx;
-  size_t f_Ag, f_S, fwd_bytes;
+  size_t f_AT, f_BT, f_S, fwd_bytes;
   size_t b_S, b_dU, b_q, b_dg, b_part, bwd_bytes;
 };
 
@@ -381,7 +381,8 @@ LrblockPlan lrblock_plan(const boost_lrblock_desc* d) {
   p.dA = choose(dt, D, G * r, T, 1, true, false);
   p.dx = choose(dt, T, D, G * r, 1, false, false);
   WsLayout f;
-  p.f_Ag = d->norm ? f.take((size_t)(D * G * r * es)) : 0;
+  p.f_AT = f.take((size_t)(D * G * r * es));
+  p.f_BT = f.take((size_t)(G * r * n * es));
   p.f_S = f.take((size_t)(T * G * r * es));
   p.fwd_bytes = f.total;
   WsLayout b;
@@ -403,34 +404,31 @@ int lrblock_fwd_impl(const boost_lrblock_desc* d, const void* x, const void* g, 
   const int64_t T = d->T, D = d->d, r = d->r, G = d->G, n = d->d_out, es = esize(dt);
   const LrblockPlan p = lrblock_plan(d);
   void* S = at(ws, p.f_S);
-  const void* Aw = A_cat;
-  if (d->norm) {
-    void* Ag = at(ws, p.f_Ag);
-    RBO_TRY(launch_gain_fold(dt, A_cat, g, Ag, D, G * r, s));
-    Aw = Ag;
-  }
+  void* AT = at(ws, p.f_AT);
+  void* BT = at(ws, p.f_BT);
+  // K-contiguous weight operands: (g * A_cat)^T [G*r, d] and B_j^T [d_out, r].
+  RBO_TRY(launch_transpose(dt, A_cat, d->norm ? g : nullptr, AT, D, G * r, 1, s));
+  RBO_TRY(launch_transpose(dt, B, nullptr, BT, r, n, G, s));
   // Down: H = rho * (x @ (g * A_cat)), S = act(H), sumsq.
   {
     GemmOps ops{};
     ops.a[0] = opnd(x, D, T, D, es);
-    ops.b[0] = opnd(Aw, G * r, D, G * r, es);
-    const float inv = d->norm ? 1.f / (float)d->d_norm : 0.f;
+    ops.b[0] = opnd(AT, D, G * r, D, es);
     if (d->norm) {
-      EpiDown<true>::Args ea{H, S, sumsq, G * r, inv, d->eps, d->act};
-      RBO_TRY((gemm<EpiDown<true>, true, false, 1>("lrblock_down", dt, p.down, T,
-                                                  G * r, D, 1, ops, ea, s)));
+      EpiDown<true>::Args ea{H, S, sumsq, G * r, 1.f / (float)d->d_norm, d->eps, d->act};
+      RBO_TRY((gemm<EpiDown<true>, true, true, 1>("lrblock_down", dt, p.down, T, G * r, D, 1, ops, ea, s)));
     } else {
       EpiDown<false>::Args ea{H, S, nullptr, G * r, 0.f, 0.f, d->act};
-      RBO_TRY((gemm<EpiDown<false>, true, false, 1>("lrblock_down", dt, p.down, T, G * r, D, 1, ops, ea, s)));
+      RBO_TRY((gemm<EpiDown<false>, true, true, 1>("lrblock_down", dt, p.down, T, G * r, D, 1, ops, ea, s)));
     }
   }
   // Up, batched over groups: Y_j = S_j @ B_j.
   {
     GemmOps ops{};
     ops.a[0] = opnd(S, G * r, T, r, es, r);
-    ops.b[0] = opnd(B, n, r, n, es, r * n);
+    ops.b[0] = opnd(BT, r, n, r, es, n * r);
     EpiStore<false>::Args ea{Y, n, T * n, nullptr};
-    RBO_TRY((gemm<EpiStore<false>, true, false, 1>("lrblock_up", dt, p.up, T, n, r, G, ops, ea, s)));
+    RBO_TRY((gemm<EpiStore<false>, true, true, 1>("lrblock_up", dt, p.up, T, n, r, G, ops, ea, s)));
   }
   return BOOST_OK;
 }
@@ -517,8 +515,8 @@ int lrmlp_check_desc(const boost_lrmlp_desc* d) {
 struct LrmlpPlan {
   Choice down1, dual, down2, up2;                       // forward
   Choice ds2, dB2, dM, rec, dA2, ds1, dB1, dA1, dx1;    // backward
-  size_t f_Ag, f_S1, f_M, f_S2, fwd_bytes;
-  size_t b_S2, b_dU2, b_dM, b_S1, b_M, b_dY, b_dU1, b_q, b_dg, b_part, bwd_bytes;
+  size_t f_A1T, f_B1T, f_A2T, f_B2T, f_S1, f_M, f_S2, fwd_bytes;
+  size_t b_B1T, b_S2, b_dU2, b_dM, b_S1, b_M, b_dY, b_dU1, b_q, b_dg, b_part, bwd_bytes;
 };
 
 LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
@@ -539,12 +537,16 @@ LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
   p.dA1 = choose(dt, D, 2 * r, T, 1, true, false);
   p.dx1 = choose(dt, T, D, 2 * r, 1, false, false);
   WsLayout f;
-  p.f_Ag = f.take((size_t)(D * 2 * r * es));
+  p.f_A1T = f.take((size_t)(D * 2 * r * es));
+  p.f_B1T = f.take((size_t)(2 * r * F * es));
+  p.f_A2T = f.take((size_t)(F * r * es));
+  p.f_B2T = f.take((size_t)(r * D * es));
   p.f_S1 = f.take((size_t)(T * 2 * r * es));
   p.f_M = f.take((size_t)(T * F * es));
   p.f_S2 = f.take((size_t)(T * r * es));
   p.fwd_bytes = f.total;
   WsLayout b;
+  p.b_B1T = b.take((size_t)(2 * r * F * es));
   p.b_S2 = b.take((size_t)(T * r * es));
   p.b_dU2 = b.take((size_t)(T * r * es));
   p.b_dM = b.take((size_t)(T * F * 4));
@@ -580,8 +582,8 @@ int btp_check_desc(const boost_btp_share_desc* d) {
 
 struct BtpPlan {
   Choice u, p, e, dA, dB, dz;
-  size_t f_ag, f_sp, fwd_bytes;
-  size_t b_e, b_du, b_ag, b_dg, b_part, bwd_bytes;
+  size_t f_BT, f_AT, f_ag, f_sp, fwd_bytes;
+  size_t b_BT, b_e, b_du, b_ag, b_dg, b_part, bwd_bytes;
 };
 
 BtpPlan btp_plan(const boost_btp_share_desc* d) {
@@ -595,10 +597,13 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   p.dB = choose(dt, r, S, T, 1, true, false);
   p.dz = choose(dt, T, r, S, 1, false, false);
   WsLayout f;
+  p.f_BT = f.take((size_t)(r * S * es));
+  p.f_AT = f.take((size_t)(S * r * es));
   p.f_ag = f.take((size_t)(T * S * es));
   p.f_sp = f.take((size_t)(p.u.tiles_n * T * 4));
   p.fwd_bytes = f.total;
   WsLayout b;
+  p.b_BT = b.take((size_t)(r * S * es));
   p.b_e = b.take((size_t)(T * S * 4));
   p.b_du = b.take((size_t)(T * S * es));
   p.b_ag = b.take((size_t)(T * S * es));
@@ -738,41 +743,48 @@ int boost_lrmlp_fwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
   RBO_TRY(check_ranges(rs));
   RBO_TRY(check_ws(ws, ws_bytes, p.fwd_bytes));
   hipStream_t s = as_stream(stream);
-  void* Ag = at(ws, p.f_Ag);
+  void* A1T = at(ws, p.f_A1T);
+  void* B1T = at(ws, p.f_B1T);
+  void* A2T = at(ws, p.f_A2T);
+  void* B2T = at(ws, p.f_B2T);
   void* S1 = at(ws, p.f_S1);
   void* M = at(ws, p.f_M);
   void* S2 = at(ws, p.f_S2);
   const float inv = 1.f / (float)D;
-  RBO_TRY(launch_gain_fold(dt, A1_cat, g, Ag, D, 2 * r, s));
+  // K-contiguous weight operands (gain folded into the first down weights).
+  RBO_TRY(launch_transpose(dt, A1_cat, g, A1T, D, 2 * r, 1, s));
+  RBO_TRY(launch_transpose(dt, B1, nullptr, B1T, r, F, 2, s));
+  RBO_TRY(launch_transpose(dt, A2, nullptr, A2T, F, r, 1, s));
+  RBO_TRY(launch_transpose(dt, B2, nullptr, B2T, r, D, 1, s));
   {  // H1 = rho * (x @ (g * A1_cat)), S1 = act(H1), sumsq
     GemmOps ops{};
     ops.a[0] = opnd(x, D, T, D, es);
-    ops.b[0] = opnd(Ag, 2 * r, D, 2 * r, es);
+    ops.b[0] = opnd(A1T, D, 2 * r, D, es);
     EpiDown<true>::Args ea{H1, S1, sumsq, 2 * r, inv, d->eps, d->act};
-    RBO_TRY((gemm<EpiDown<true>, true, false, 1>("mlp_down1", dt, p.down1, T, 2 * r, D, 1, ops, ea, s)));
+    RBO_TRY((gemm<EpiDown<true>, true, true, 1>("mlp_down1", dt, p.down1, T, 2 * r, D, 1, ops, ea, s)));
   }
   {  // M = SiLU(S1_0 @ B1_0) * (S1_1 @ B1_1)
     GemmOps ops{};
     ops.a[0] = opnd(S1, 2 * r, T, r, es);
     ops.a[1] = opnd(static_cast<const char*>(S1) + r * es, 2 * r, T, r, es);
-    ops.b[0] = opnd(B1, F, r, F, es);
-    ops.b[1] = opnd(static_cast<const char*>(B1) + r * F * es, F, r, F, es);
+    ops.b[0] = opnd(B1T, r, F, r, es);
+    ops.b[1] = opnd(static_cast<const char*>(B1T) + F * r * es, r, F, r, es);
     EpiSwiglu::Args ea{M, F};
-    RBO_TRY((gemm<EpiSwiglu, true, false, 2>("mlp_up1_swiglu", dt, p.dual, T, F, r, 1, ops, ea, s)));
+    RBO_TRY((gemm<EpiSwiglu, true, true, 2>("mlp_up1_swiglu", dt, p.dual, T, F, r, 1, ops, ea, s)));
   }
   {  // H2 = M @ A2, S2 = act(H2)
     GemmOps ops{};
     ops.a[0] = opnd(M, F, T, F, es);
-    ops.b[0] = opnd(A2, r, F, r, es);
+    ops.b[0] = opnd(A2T, F, r, F, es);
     EpiDown<false>::Args ea{H2, S2, nullptr, r, 0.f, 0.f, d->act};
-    RBO_TRY((gemm<EpiDown<false>, true, false, 1>("mlp_down2", dt, p.down2, T, r, F, 1, ops, ea, s)));
+    RBO_TRY((gemm<EpiDown<false>, true, true, 1>("mlp_down2", dt, p.down2, T, r, F, 1, ops, ea, s)));
   }
   {  // Y = S2 @ B2
     GemmOps ops{};
     ops.a[0] = opnd(S2, r, T, r, es);
-    ops.b[0] = opnd(B2, D, r, D, es);
+    ops.b[0] = opnd(B2T, r, D, r, es);
     EpiStore<false>::Args ea{Y, D, 0, nullptr};
-    RBO_TRY((gemm<EpiStore<false>, true, false, 1>("mlp_up2", dt, p.up2, T, D, r, 1, ops, ea, s)));
+    RBO_TRY((gemm<EpiStore<false>, true, true, 1>("mlp_up2", dt, p.up2, T, D, r, 1, ops, ea, s)));
   }
   return BOOST_OK;
 }
@@ -841,14 +853,16 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
   }
   // S1 = act(H1) recomputed from the saved bottleneck.
   RBO_TRY(launch_act_quant(dt, H1, S1, T * 2 * r, d->act, s));
+  void* B1T = at(ws, p.b_B1T);
+  RBO_TRY(launch_transpose(dt, B1, nullptr, B1T, r, F, 2, s));
   {  // recompute Yg, Yu; M, dYg, dYu
     GemmOps ops{};
     ops.a[0] = opnd(S1, 2 * r, T, r, es);
     ops.a[1] = opnd(static_cast<const char*>(S1) + r * es, 2 * r, T, r, es);
-    ops.b[0] = opnd(B1, F, r, F, es);
-    ops.b[1] = opnd(static_cast<const char*>(B1) + r * F * es, F, r, F, es);
+    ops.b[0] = opnd(B1T, r, F, r, es);
+    ops.b[1] = opnd(static_cast<const char*>(B1T) + F * r * es, r, F, r, es);
     EpiSwigluBwd::Args ea{dM, Mr, dYgu, F, T * F};
-    RBO_TRY((gemm<EpiSwigluBwd, true, false, 2>("mlp_recompute_swiglu_bwd", dt, p.rec, T, F, r, 1, ops, ea, s)));
+    RBO_TRY((gemm<EpiSwigluBwd, true, true, 2>("mlp_recompute_swiglu_bwd", dt, p.rec, T, F, r, 1, ops, ea, s)));
   }
   {  // dA2 = M^T @ dU2
     GemmOps ops{};
@@ -891,21 +905,25 @@ int boost_btp_share_fwd(const boost_btp_share_desc* d, const void* z, const void
   RBO_TRY(check_ranges(rs));
   RBO_TRY(check_ws(ws, ws_bytes, p.fwd_bytes));
   hipStream_t st = as_stream(stream);
+  void* BT = at(ws, p.f_BT);
+  void* AT = at(ws, p.f_AT);
   void* ag = at(ws, p.f_ag);
   float* sp = reinterpret_cast<float*>(at(ws, p.f_sp));
+  RBO_TRY(launch_transpose(dt, B_s, nullptr, BT, r, S, 1, st));
+  RBO_TRY(launch_transpose(dt, A_s, nullptr, AT, S, r, 1, st));
   {  // u = z @ B_s; a = SiLU(u); ag = a * g_s; row partials of a^2
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);
-    ops.b[0] = opnd(B_s, S, r, S, es);
+    ops.b[0] = opnd(BT, r, S, r, es);
     EpiBtpU::Args ea{g_s, ag, sp, T, S};
-    RBO_TRY((gemm<EpiBtpU, true, false, 1>("btp_u", dt, p.u, T, S, r, 1, ops, ea, st)));
+    RBO_TRY((gemm<EpiBtpU, true, true, 1>("btp_u", dt, p.u, T, S, r, 1, ops, ea, st)));
   }
   {  // p = ag @ A_s; s = sum of the partials
     GemmOps ops{};
     ops.a[0] = opnd(ag, S, T, S, es);
-    ops.b[0] = opnd(A_s, r, S, r, es);
+    ops.b[0] = opnd(AT, S, r, S, es);
     EpiBtpP::Args ea{pout, r, sp, p.u.tiles_n, T, s_out};
-    RBO_TRY((gemm<EpiBtpP, true, false, 1>("btp_p", dt, p.p, T, r, S, 1, ops, ea, st)));
+    RBO_TRY((gemm<EpiBtpP, true, true, 1>("btp_p", dt, p.p, T, r, S, 1, ops, ea, st)));
   }
   return BOOST_OK;
 }
@@ -947,12 +965,14 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
     EpiStore<true>::Args ea{e, S, 0, nullptr};
     RBO_TRY((gemm<EpiStore<true>, true, true, 1>("btp_e", dt, p.e, T, S, r, 1, ops, ea, st)));
   }
+  void* BT = at(ws, p.b_BT);
+  RBO_TRY(launch_transpose(dt, B_s, nullptr, BT, r, S, 1, st));
   {  // recompute u = z @ B_s; du, ag, dg partials
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);
-    ops.b[0] = opnd(B_s, S, r, S, es);
+    ops.b[0] = opnd(BT, r, S, r, es);
     EpiBtpUBwd::Args ea{e, ds, g_s, du, ag, dgp, S};
-    RBO_TRY((gemm<EpiBtpUBwd, true, false, 1>("btp_u_bwd", dt, p.u, T, S, r, 1, ops, ea, st)));
+    RBO_TRY((gemm<EpiBtpUBwd, true, true, 1>("btp_u_bwd", dt, p.u, T, S, r, 1, ops, ea, st)));
   }
   RBO_TRY(launch_colsum(dgp, p.u.tiles_m, S, S, dg_s, st));
   {  // dA_s = ag^T @ dp

@@ -125,6 +125,22 @@ template <> struct Mfma<float> {
   }
 };
 
+// Sum of squares of one MFMA A fragment, accumulated into acc.
+__device__ __forceinline__ float frag_sumsq(bf16x8 f, float acc) {
+  const u32x4 v = __builtin_bit_cast(u32x4, f);
+  // Words are copied to scalars first: bit-casting a vector element selected
+  // by a loop index straight into the dot2 builtin makes this compiler read
+  // word 0 every time.
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x2 p = __builtin_bit_cast(bf16x2, w[q]);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_sumsq(float f, float acc) { return __builtin_fmaf(f, f, acc); }
+
 // ---------------------------------------------------------------------------
 // Tile configuration
 // ---------------------------------------------------------------------------
@@ -141,7 +157,14 @@ struct Cfg {
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int PIPE_BYTES = 2 * STAGE_BYTES;
+  static constexpr int NW = WM * WN;
+  // Operands that are K-contiguous on both sides are loaded straight into
+  // LDS; three stages where they fit next to the epilogue vectors in the
+  // 160 KB of a CU, otherwise two. The register-staged path uses two.
+  static constexpr bool DIRECT = AKC_ && BKC_;
+  static constexpr int VEC_BYTES_ = (BM + BN + WN * BM + WM * BN) * 4;
+  static constexpr int NSTAGE = (DIRECT && 3 * STAGE_BYTES + VEC_BYTES_ <= 160 * 1024) ? 3 : 2;
+  static constexpr int PIPE_BYTES = NSTAGE * STAGE_BYTES;
   // Epilogue staging: each wave writes 32 accumulator rows at a time (per
   // accumulator) into a private fp32 buffer with a row stride padded by 8
   // floats (the two half-waves of the MFMA layout then hit disjoint banks),
@@ -151,8 +174,9 @@ struct Cfg {
   static constexpr int EPI_BYTES = WM * WN * NACC * EPI_SUB * 4;
   static constexpr int SCR_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
   // After that: per-row / per-column fp32 vectors and reduction partials.
-  static constexpr int VEC_BYTES = (BM + BN + WN * BM + WM * BN) * 4;
+  static constexpr int VEC_BYTES = VEC_BYTES_;
   static constexpr int LDS_BYTES = SCR_BYTES + VEC_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "tile does not fit the LDS of a CU");
   static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA block");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
 };
@@ -334,6 +358,39 @@ struct Loader {
 };
 
 // ---------------------------------------------------------------------------
+// Direct-to-LDS loader for a K-contiguous operand. One buffer_load_dwordx4
+// with the LDS flag writes 64 lanes x 16 bytes to LDS at a wave-uniform base
+// (lane l at base + 16 l), i.e. 8 consecutive 128-byte tile rows. Lane l
+// therefore fetches the global chunk that the XOR swizzle places at position
+// l & 7 of row l >> 3. The data never passes through registers.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <class C, int ROWS>
+struct DirectLoader {
+  static constexpr int INSTR = ROWS / 8 / C::NW;  // per wave per K slab
+  static_assert(ROWS % (8 * C::NW) == 0, "direct loader: rows must split evenly over the waves");
+  __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int k0, char* tile,
+                                               int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < INSTR; ++q) {
+      const int row0 = 8 * (q * C::NW + wave);
+      const int row = row0 + (lane >> 3);
+      const int chunk = (lane & 7) ^ lds_swz(row);
+      const uint32_t off = (uint32_t)(row * ld_bytes) + (uint32_t)((k0 + chunk * C::VEC) * C::ES);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + row0 * kRowBytes), 16, off, 0, 0, 0);
+    }
+  }
+};
+
+// s_waitcnt vmcnt(n) with the other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
 // Block -> tile mapping. Workgroups are handed to the 8 XCDs round-robin;
 // the remap gives each XCD a contiguous range of logical tiles, and tiles are
 // walked in groups of 8 tile rows so neighbours share A rows and B columns in
@@ -470,7 +527,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
   typedef Mfma<T> MF;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool RSS = E::kRowSumsq;
-  static_assert(!RSS || C::AKC, "row statistics need a K-contiguous A");
+  static_assert(!RSS || C::NACC == 1, "row statistics are taken in single-accumulator products");
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -497,9 +554,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[p][i][j][v] = 0.f;
 
-  Loader<C, C::BM, C::AKC, false, RSS> la;
+  Loader<C, C::BM, C::AKC, false, false> la;
   Loader<C, C::BN, C::BKC, true, false> lb;
-  la.init();
+  constexpr int KK = C::BK / MF::KI;
+  // Online-RMSNorm statistic: sums of squares of the A rows, taken from the
+  // MFMA A fragments (each lane holds 8 k-values of one row per sub-step).
+  float ss[C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) ss[i] = 0.f;
 
   static_for<0, C::NACC>([&](auto p) {
     const Operand& A = ops.a[p];
@@ -514,23 +576,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(static_cast<const char*>(B.ptr) + b_off, B.extent - ((int64_t)n0 * (C::BKC ? B.ld : 1) * C::ES));
     const int64_t lda_b = A.ld * C::ES, ldb_b = B.ld * C::ES;
+    const int kl = (lane >> 5) * MF::KL;
 
-    la.fetch(ra, lda_b, kbeg, t);
-    lb.fetch(rb, ldb_b, kbeg, t);
-    la.store(smem, t);
-    lb.store(smem + C::A_BYTES, t);
-    la.fetch(ra, lda_b, kbeg + C::BK, t);
-    lb.fetch(rb, ldb_b, kbeg + C::BK, t);
-
-    constexpr int KK = C::BK / MF::KI;
-    for (int kt = 0; kt < KT; ++kt) {
-      __syncthreads();
-      const char* As = smem + (kt & 1) * C::STAGE_BYTES;
-      const char* Bs = As + C::A_BYTES;
-      char* Ns = smem + ((kt & 1) ^ 1) * C::STAGE_BYTES;
-      const bool next_in_k = kt + 1 < KT;
+    // MFMAs of one LDS stage; `stage_work(kk)` runs after sub-step kk's
+    // MFMAs have been issued (staging of the register path).
+    auto compute = [&](const char* As, const char* Bs, auto&& stage_work) {
       typename MF::Frag fa[2][C::FM], fb[2][C::FN];
-      const int kl = (lane >> 5) * MF::KL;
       static_for<0, C::FM>([&](auto i) { fa[0][i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), kl); });
       static_for<0, C::FN>([&](auto j) { fb[0][j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), kl); });
       static_for<0, KK>([&](auto kk) {
@@ -543,39 +594,93 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
         static_for<0, C::FM>([&](auto i) {
           static_for<0, C::FN>([&](auto j) { acc[p][i][j] = MF::mma(fa[cur][i], fb[cur][j], acc[p][i][j]); });
         });
+        if constexpr (RSS) static_for<0, C::FM>([&](auto i) { ss[i] = frag_sumsq(fa[cur][i], ss[i]); });
+        stage_work(kk);
+      });
+    };
+
+    if constexpr (C::DIRECT) {
+      typedef DirectLoader<C, C::BM> DA;
+      typedef DirectLoader<C, C::BN> DB;
+      constexpr int L = DA::INSTR + DB::INSTR;  // loads per wave per K slab
+      auto issue = [&](int ks, int stage) {
+        char* st = smem + stage * C::STAGE_BYTES;
+        DA::issue(ra, lda_b, kbeg + ks * C::BK, st, wave, lane);
+        DB::issue(rb, ldb_b, kbeg + ks * C::BK, st + C::A_BYTES, wave, lane);
+      };
+      issue(0, 0);
+      if constexpr (C::NSTAGE == 3) {
+        if (KT > 1) issue(1, 1);
+      }
+      for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt % C::NSTAGE;
+        if constexpr (C::NSTAGE == 3) {
+          // Slabs kt and kt+1 may be in flight; wait for kt's only.
+          if (kt + 1 < KT) wait_vmcnt<L>(); else wait_vmcnt<0>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        // A plain s_barrier: __syncthreads() would add a release fence that
+        // waits for every outstanding load, including the slab still allowed
+        // in flight. The empty asm statements keep the compiler from moving
+        // LDS accesses across the barrier.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // The stage refilled now was last read in step kt-1 (three stages:
+        // slab kt+2) or is the one just released (two stages: slab kt+1).
+        if constexpr (C::NSTAGE == 3) {
+          if (kt + 2 < KT) issue(kt + 2, (kt + 2) % 3);
+        } else {
+          if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
+        }
+        const char* As = smem + cur * C::STAGE_BYTES;
+        compute(As, As + C::A_BYTES, [](auto) {});
+      }
+      __syncthreads();
+    } else {
+      la.fetch(ra, lda_b, kbeg, t);
+      lb.fetch(rb, ldb_b, kbeg, t);
+      la.store(smem, t);
+      lb.store(smem + C::A_BYTES, t);
+      la.fetch(ra, lda_b, kbeg + C::BK, t);
+      lb.fetch(rb, ldb_b, kbeg + C::BK, t);
+      for (int kt = 0; kt < KT; ++kt) {
+        __syncthreads();
+        const char* As = smem + (kt & 1) * C::STAGE_BYTES;
+        char* Ns = smem + ((kt & 1) ^ 1) * C::STAGE_BYTES;
         // Staging work after the first two sub-steps' MFMAs have been issued:
         // each operand's slab for step kt+1 goes to the other LDS stage and
         // its registers are refilled at once with step kt+2, so every global
         // load has a whole K step to land. The scheduling barriers keep the
         // compiler from sinking the loads to the end of the step.
-        if constexpr (kk == 0 || kk == 1) {
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (kk == 0) {
-            la.store(Ns, t, next_in_k);
-            la.fetch(ra, lda_b, kbeg + (kt + 2) * C::BK, t);
-          } else {
-            lb.store(Ns + C::A_BYTES, t);
-            lb.fetch(rb, ldb_b, kbeg + (kt + 2) * C::BK, t);
+        compute(As, As + C::A_BYTES, [&](auto kk) {
+          if constexpr (kk == 0 || kk == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kk == 0) {
+              la.store(Ns, t);
+              la.fetch(ra, lda_b, kbeg + (kt + 2) * C::BK, t);
+            } else {
+              lb.store(Ns + C::A_BYTES, t);
+              lb.fetch(rb, ldb_b, kbeg + (kt + 2) * C::BK, t);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      });
+        });
+      }
+      __syncthreads();
     }
-    __syncthreads();
   });
 
   float* rowv = reinterpret_cast<float*>(smem + C::SCR_BYTES);
   float* colv = rowv + C::BM;
   if constexpr (RSS) {
-    // Row sums of squares of A (the Online-RMSNorm statistic): the 8 lanes
-    // holding the 8 chunks of a row reduce, lane 0 of the 8 publishes.
+    // Lanes l and l+32 hold the two k halves of the same row; waves in the
+    // same wave row saw the same A rows, so wave column 0 publishes.
 #pragma unroll
-    for (int u = 0; u < decltype(la)::KC_UNITS; ++u) {
-      float s = la.ss[u];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      if ((t & 7) == 0) rowv[(t >> 3) + u * (C::NT / 8)] = s;
+    for (int i = 0; i < C::FM; ++i) {
+      const float s = ss[i] + __shfl_xor(ss[i], 32);
+      if (wn == 0 && lane < 32) rowv[wm * C::WTM + i * 32 + lane] = s;
     }
     __syncthreads();
   }
