@@ -584,6 +584,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
       typename MF::Frag fa[2][C::FM], fb[2][C::FN];
       static_for<0, C::FM>([&](auto i) { fa[0][i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), kl); });
       static_for<0, C::FN>([&](auto j) { fb[0][j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), kl); });
+      __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);  // sub-step 0's reads lead
       static_for<0, KK>([&](auto kk) {
         constexpr int cur = kk & 1, nxt = cur ^ 1;
         if constexpr (kk + 1 < KK) {
@@ -594,6 +595,11 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
         static_for<0, C::FM>([&](auto i) {
           static_for<0, C::FN>([&](auto j) { acc[p][i][j] = MF::mma(fa[cur][i], fb[cur][j], acc[p][i][j]); });
         });
+        // Issue order: every fragment read of sub-step kk+1, then the MFMAs of
+        // sub-step kk, so the reads have a whole sub-step of MFMAs to land
+        // (left alone, the scheduler issues each read just before its use).
+        if constexpr (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
         if constexpr (RSS) static_for<0, C::FM>([&](auto i) { ss[i] = frag_sumsq(fa[cur][i], ss[i]); });
         stage_work(kk);
       });
