@@ -21,22 +21,28 @@
 // LDS layout: each staged tile row holds 128 bytes of K (BK = 64 bf16 or
 // 32 fp32). 16-byte chunk c of row m lives at chunk c ^ ((m ^ (m>>3)) & 7):
 // MFMA fragment reads (8 consecutive rows, same chunk) and transposed
-// writes (rows 8 apart, same chunk) both hit 8 distinct chunks.
+// writes (rows 8 apart, same chunk) both hit 8 distinct chunks. Rows of 128
+// bytes also keep every global request one full cache line: with 64-byte
+// rows the same slab streams measurably slower.
 //
 // Global loads use buffer instructions with a per-operand byte range, so
 // every read past the end of a tensor returns zero: rows past T and the
 // K tail of K = tokens products need no branches. Reads past M or N inside
 // the tensor only feed accumulator rows/columns that the epilogue masks.
 //
-// Pipelining: two LDS stages and one set of staging registers. During K step
-// kt the MFMAs read stage kt%2 while the slab of step kt+1 (already in the
-// staging registers since the previous step) is written to the other stage
-// and the slab of step kt+2 is fetched from HBM, so each global load has a
-// whole K step to land. MFMA fragments are double-buffered across the
-// 16-wide k sub-steps. The loop body has no branches (the slabs past the end
-// of K are read through the buffer range check and never consumed), which
-// lets the scheduler interleave LDS, global and MFMA work; one barrier per
-// K step.
+// Pipelining. When both operands are K-contiguous, each K slab goes from
+// global memory straight into LDS (buffer loads with the LDS flag), with as
+// many LDS stages as fit (two for 256 x 256 tiles, three or four for smaller
+// ones): while the MFMAs read stage kt, the slabs of the next NSTAGE-1 steps
+// are in flight, and each step waits only for the oldest. The load
+// instructions of the next slab are interleaved one by one with the MFMAs of
+// the first two k sub-steps, so that a stalled load issue never leaves the
+// matrix cores idle (with one wave per SIMD there is no other wave to fill
+// the gap). Otherwise operands pass through registers (to be transposed)
+// with two LDS stages: during step kt the slab of step kt+1, already in
+// registers, is written to the other stage and the slab of step kt+2 is
+// fetched. MFMA fragments are double-buffered across the 16-wide k
+// sub-steps; one barrier per K step.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -52,8 +58,6 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kRowBytes = 128;  // bytes of K per staged tile row
-
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i = B..E-1. Used
@@ -66,6 +70,8 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
+
+constexpr int kRowBytes = 128;  // bytes of K per staged tile row
 
 __device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -150,20 +156,25 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NACC = NACC_;
   static constexpr bool AKC = AKC_, BKC = BKC_;
   static constexpr int NT = WM * WN * 64;
+  static constexpr int NW = WM * WN;
   static constexpr int ES = sizeof(T);
   static constexpr int VEC = 16 / ES;
-  static constexpr int BK = kRowBytes / ES;
+  // Operands that are K-contiguous on both sides are loaded straight into
+  // LDS; the others pass through registers.
+  static constexpr bool DIRECT = AKC_ && BKC_;
+  static constexpr int RB = kRowBytes;
+  static constexpr int CH = RB / 16;  // 16-byte chunks per row
+  static constexpr int BK = RB / ES;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int NW = WM * WN;
-  // Operands that are K-contiguous on both sides are loaded straight into
-  // LDS; three stages where they fit next to the epilogue vectors in the
-  // 160 KB of a CU, otherwise two. The register-staged path uses two.
-  static constexpr bool DIRECT = AKC_ && BKC_;
+  // The direct path takes as many stages (up to four) as fit next to the
+  // epilogue vectors in the 160 KB of a CU; the register path uses two.
   static constexpr int VEC_BYTES_ = (BM + BN + WN * BM + WM * BN) * 4;
-  static constexpr int NSTAGE = (DIRECT && 3 * STAGE_BYTES + VEC_BYTES_ <= 160 * 1024) ? 3 : 2;
+  static constexpr int FIT_ = (160 * 1024 - VEC_BYTES_) / STAGE_BYTES;
+  static constexpr int NSTAGE = DIRECT ? (FIT_ < 4 ? FIT_ : 4) : 2;
+  static_assert(NSTAGE >= 2, "two pipeline stages must fit in LDS");
   static constexpr int PIPE_BYTES = NSTAGE * STAGE_BYTES;
   // Epilogue staging: each wave writes 32 accumulator rows at a time (per
   // accumulator) into a private fp32 buffer with a row stride padded by 8
@@ -236,13 +247,14 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 template <class C, int ROWS, bool KC, bool FROM_TOP, bool ROWSUMSQ>
 struct Loader {
   static constexpr int VEC = C::VEC;
-  // KC: ROWS*8 chunks; thread t takes chunk t&7 of rows (t>>3) + u*(NT/8).
-  static constexpr int KC_UNITS = (ROWS * 8) / C::NT;
+  // KC: ROWS*CH chunks; thread t takes chunk t%CH of rows t/CH + u*(NT/CH).
+  static constexpr int CH = C::CH;
+  static constexpr int KC_UNITS = (ROWS * CH) / C::NT;
   // transposed: (BK/VEC) x (ROWS/VEC) blocks of VEC x VEC elements.
   static constexpr int BLOCKS = (C::BK / VEC) * (ROWS / VEC);
   static constexpr int T_UNITS = cdiv(BLOCKS, C::NT);
   static constexpr int NREG = KC ? KC_UNITS : T_UNITS * VEC;
-  static_assert(!KC || (ROWS * 8) % C::NT == 0, "KC loader: ROWS*8 must divide by NT");
+  static_assert(!KC || (ROWS * CH) % C::NT == 0, "KC loader: ROWS*CH must divide by NT");
   static_assert(!KC || KC_UNITS >= 1, "KC loader: too few rows");
 
   u32x4 r[NREG];
@@ -256,10 +268,10 @@ struct Loader {
   // Issue the global reads of the slab starting at column/row k0.
   __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int k0, int t) {
     if constexpr (KC) {
-      const int c = t & 7;
+      const int c = t % CH;
 #pragma unroll
       for (int u = 0; u < KC_UNITS; ++u) {
-        const int row = (t >> 3) + u * (C::NT / 8);
+        const int row = t / CH + u * (C::NT / CH);
         const uint32_t off = (uint32_t)(row * ld_bytes) + (uint32_t)((k0 + c * VEC) * C::ES);
         r[u] = buf_load16(rs, off);
       }
@@ -287,10 +299,10 @@ struct Loader {
   // not enter the row statistics).
   __device__ __forceinline__ void store(char* tile, int t, bool count = true) {
     if constexpr (KC) {
-      const int c = t & 7;
+      const int c = t % CH;
 #pragma unroll
       for (int u = 0; u < KC_UNITS; ++u) {
-        const int row = (t >> 3) + u * (C::NT / 8);
+        const int row = t / CH + u * (C::NT / CH);
         *reinterpret_cast<u32x4*>(tile + lds_off(row, c)) = r[u];
         if constexpr (ROWSUMSQ) {
           const float add = sumsq16(r[u], 0.f);
@@ -360,25 +372,29 @@ struct Loader {
 // ---------------------------------------------------------------------------
 // Direct-to-LDS loader for a K-contiguous operand. One buffer_load_dwordx4
 // with the LDS flag writes 64 lanes x 16 bytes to LDS at a wave-uniform base
-// (lane l at base + 16 l), i.e. 8 consecutive 128-byte tile rows. Lane l
+// (lane l at base + 16 l), i.e. 1024/RB consecutive tile rows. Lane l
 // therefore fetches the global chunk that the XOR swizzle places at position
-// l & 7 of row l >> 3. The data never passes through registers.
+// l % CH of row l / CH. The data never passes through registers.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <class C, int ROWS>
 struct DirectLoader {
-  static constexpr int INSTR = ROWS / 8 / C::NW;  // per wave per K slab
-  static_assert(ROWS % (8 * C::NW) == 0, "direct loader: rows must split evenly over the waves");
+  static constexpr int RPI = 1024 / C::RB;          // tile rows per instruction
+  static constexpr int INSTR = ROWS / RPI / C::NW;  // per wave per K slab
+  static_assert(ROWS % (RPI * C::NW) == 0, "direct loader: rows must split evenly over the waves");
+  // oob = 0 loads the slab; oob = 0x80000000 pushes every offset past the
+  // buffer range, so the instructions still issue (keeping the loop free of
+  // branches) but fetch nothing.
   __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int k0, char* tile,
-                                               int wave, int lane) {
+                                               int wave, int lane, uint32_t oob = 0) {
 #pragma unroll
     for (int q = 0; q < INSTR; ++q) {
-      const int row0 = 8 * (q * C::NW + wave);
-      const int row = row0 + (lane >> 3);
-      const int chunk = (lane & 7) ^ lds_swz(row);
-      const uint32_t off = (uint32_t)(row * ld_bytes) + (uint32_t)((k0 + chunk * C::VEC) * C::ES);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + row0 * kRowBytes), 16, off, 0, 0, 0);
+      const int row0 = RPI * (q * C::NW + wave);
+      const int row = row0 + lane / C::CH;
+      const int chunk = (lane % C::CH) ^ lds_swz(row);
+      const uint32_t off = ((uint32_t)(row * ld_bytes) + (uint32_t)((k0 + chunk * C::VEC) * C::ES)) | oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + row0 * C::RB), 16, off, 0, 0, 0);
     }
   }
 };
@@ -389,6 +405,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// Load instructions a K step interleaves with the MFMAs of sub-steps 0 and 1.
+template <int V0, int V1>
+struct SlabPlan {
+  static constexpr int at(int kk) { return kk == 0 ? V0 : (kk == 1 ? V1 : 0); }
+};
 
 // ---------------------------------------------------------------------------
 // Block -> tile mapping. Workgroups are handed to the 8 XCDs round-robin;
@@ -578,15 +600,20 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
     const int64_t lda_b = A.ld * C::ES, ldb_b = B.ld * C::ES;
     const int kl = (lane >> 5) * MF::KL;
 
-    // MFMAs of one LDS stage; `stage_work(kk)` runs after sub-step kk's
-    // MFMAs have been issued (staging of the register path).
-    auto compute = [&](const char* As, const char* Bs, auto&& stage_work) {
+    // MFMAs of one LDS stage. With NV = 0, `stage_work(kk)` runs after
+    // sub-step kk's MFMAs have been issued (staging of the register path).
+    // With NV > 0, stage_work(kk) issues NV(kk) global->LDS load
+    // instructions (the first two sub-steps), which are interleaved one by
+    // one with that sub-step's MFMAs.
+    auto compute = [&](const char* As, const char* Bs, auto nv_tag, auto&& stage_work) {
+      typedef decltype(nv_tag) NV;
       typename MF::Frag fa[2][C::FM], fb[2][C::FN];
       static_for<0, C::FM>([&](auto i) { fa[0][i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), kl); });
       static_for<0, C::FN>([&](auto j) { fb[0][j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), kl); });
       __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);  // sub-step 0's reads lead
       static_for<0, KK>([&](auto kk) {
         constexpr int cur = kk & 1, nxt = cur ^ 1;
+        constexpr int nv = NV::at(kk);
         if constexpr (kk + 1 < KK) {
           const int k = (kk + 1) * MF::KI + kl;
           static_for<0, C::FM>([&](auto i) { fa[nxt][i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), k); });
@@ -595,13 +622,24 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
         static_for<0, C::FM>([&](auto i) {
           static_for<0, C::FN>([&](auto j) { acc[p][i][j] = MF::mma(fa[cur][i], fb[cur][j], acc[p][i][j]); });
         });
+        if constexpr (nv > 0) stage_work(kk);
         // Issue order: every fragment read of sub-step kk+1, then the MFMAs of
-        // sub-step kk, so the reads have a whole sub-step of MFMAs to land
-        // (left alone, the scheduler issues each read just before its use).
+        // sub-step kk (with the slab loads, if any, one after every few
+        // MFMAs), so the reads have a whole sub-step of MFMAs to land (left
+        // alone, the scheduler issues each read just before its use).
         if constexpr (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
+        if constexpr (nv > 0) {
+          constexpr int NM = C::FM * C::FN;
+          static_for<0, nv>([&](auto v) {
+            constexpr int m = (NM * (v + 1)) / nv - (NM * v) / nv;  // MFMAs after load v
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+          });
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
+        }
         if constexpr (RSS) static_for<0, C::FM>([&](auto i) { ss[i] = frag_sumsq(fa[cur][i], ss[i]); });
-        stage_work(kk);
+        if constexpr (nv == 0) stage_work(kk);
       });
     };
 
@@ -609,40 +647,44 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
       typedef DirectLoader<C, C::BM> DA;
       typedef DirectLoader<C, C::BN> DB;
       constexpr int L = DA::INSTR + DB::INSTR;  // loads per wave per K slab
-      auto issue = [&](int ks, int stage) {
-        char* st = smem + stage * C::STAGE_BYTES;
-        DA::issue(ra, lda_b, kbeg + ks * C::BK, st, wave, lane);
-        DB::issue(rb, ldb_b, kbeg + ks * C::BK, st + C::A_BYTES, wave, lane);
-      };
-      issue(0, 0);
-      if constexpr (C::NSTAGE == 3) {
-        if (KT > 1) issue(1, 1);
-      }
+      constexpr int NS = C::NSTAGE;
+      // Every step issues exactly one slab (past the end of K, out of range),
+      // so L * (NS-2) loads still outstanding means slab kt has landed.
+      static_for<0, NS - 1>([&](auto s) {
+        const uint32_t oob = s() < KT ? 0u : 0x80000000u;
+        char* st = smem + s() * C::STAGE_BYTES;
+        DA::issue(ra, lda_b, kbeg + s() * C::BK, st, wave, lane, oob);
+        DB::issue(rb, ldb_b, kbeg + s() * C::BK, st + C::A_BYTES, wave, lane, oob);
+      });
+      int cur = 0;       // stage read in this step
+      int nxt = NS - 1;  // stage refilled in this step
       for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt % C::NSTAGE;
-        if constexpr (C::NSTAGE == 3) {
-          // Slabs kt and kt+1 may be in flight; wait for kt's only.
-          if (kt + 1 < KT) wait_vmcnt<L>(); else wait_vmcnt<0>();
-        } else {
-          wait_vmcnt<0>();
-        }
+        // Slabs kt .. kt+NS-2 are in flight; wait for slab kt only.
+        wait_vmcnt<L * (NS - 2)>();
         // A plain s_barrier: __syncthreads() would add a release fence that
-        // waits for every outstanding load, including the slab still allowed
-        // in flight. The empty asm statements keep the compiler from moving
-        // LDS accesses across the barrier.
+        // waits for every outstanding load, including the slabs still
+        // allowed in flight. The empty asm statements keep the compiler from
+        // moving LDS accesses across the barrier.
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // The stage refilled now was last read in step kt-1 (three stages:
-        // slab kt+2) or is the one just released (two stages: slab kt+1).
-        if constexpr (C::NSTAGE == 3) {
-          if (kt + 2 < KT) issue(kt + 2, (kt + 2) % 3);
-        } else {
-          if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
-        }
+        // Slab kt+NS-1 goes to the stage last read in step kt-1, which every
+        // wave has finished once past the barrier. Past the end of K the
+        // loads are issued out of range and fetch nothing.
+        const int ks = kt + NS - 1;
+        const uint32_t oob = ks < KT ? 0u : 0x80000000u;
+        char* st = smem + nxt * C::STAGE_BYTES;
         const char* As = smem + cur * C::STAGE_BYTES;
-        compute(As, As + C::A_BYTES, [](auto) {});
+        compute(As, As + C::A_BYTES, SlabPlan<DA::INSTR, DB::INSTR>{}, [&](auto kk) {
+          if constexpr (kk == 0) DA::issue(ra, lda_b, kbeg + ks * C::BK, st, wave, lane, oob);
+          if constexpr (kk == 1) DB::issue(rb, ldb_b, kbeg + ks * C::BK, st + C::A_BYTES, wave, lane, oob);
+        });
+        cur = cur + 1 == NS ? 0 : cur + 1;
+        nxt = nxt + 1 == NS ? 0 : nxt + 1;
       }
+      // Out-of-range loads still count; none may land after the epilogue
+      // starts reusing this LDS.
+      wait_vmcnt<0>();
       __syncthreads();
     } else {
       la.fetch(ra, lda_b, kbeg, t);
@@ -660,7 +702,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
         // its registers are refilled at once with step kt+2, so every global
         // load has a whole K step to land. The scheduling barriers keep the
         // compiler from sinking the loads to the end of the step.
-        compute(As, As + C::A_BYTES, [&](auto kk) {
+        compute(As, As + C::A_BYTES, SlabPlan<0, 0>{}, [&](auto kk) {
           if constexpr (kk == 0 || kk == 1) {
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (kk == 0) {
