@@ -12,37 +12,40 @@
 //   A "KC": element (m,k) at m*ld + k  (activations x, dY, S, ...)
 //   A "MC": element (m,k) at k*ld + m  (transposed activations, K = tokens)
 //   B "KC": element (k,n) at n*ld + k  (a weight used transposed)
-//   B "NC": element (k,n) at k*ld + n  (a weight in [in,out] layout, or an
-//           activation when K = tokens)
-// KC operands are copied to LDS in 16-byte chunks. MC/NC operands are loaded
-// as VEC x VEC blocks (VEC elements per 16 bytes), transposed in registers,
-// and written K-contiguous, so the MFMA loop only ever sees one LDS layout.
+//   B "NC": element (k,n) at k*ld + n  (an activation when K = tokens)
+// Every operand is copied from global memory straight into LDS (buffer
+// loads with the LDS flag, 16 bytes per lane) in its own layout; the MFMA
+// fragments are formed by the LDS reads.
 //
-// LDS layout: each staged tile row holds 128 bytes of K (BK = 64 bf16 or
-// 32 fp32). 16-byte chunk c of row m lives at chunk c ^ ((m ^ (m>>3)) & 7):
-// MFMA fragment reads (8 consecutive rows, same chunk) and transposed
-// writes (rows 8 apart, same chunk) both hit 8 distinct chunks. Rows of 128
-// bytes also keep every global request one full cache line: with 64-byte
-// rows the same slab streams measurably slower.
+// LDS layouts (16-byte chunks, XOR-swizzled so that both the fragment reads
+// and the global requests stay conflict-free and full-line):
+//   KC: one 128-byte row of K per tile row (BK = 64 bf16 / 32 fp32); chunk
+//       c of row m at c ^ ((m ^ (m>>3)) & 7). A fragment read (8 rows, one
+//       chunk) hits 8 distinct chunks.
+//   MC/NC: one row of the tile's M (or N) extent per k; chunk c of row k at
+//       c ^ (4 (k & 3)) for bf16 and c ^ (8 (k & 1)) for fp32. bf16
+//       fragments come from the gfx950 transposing LDS read
+//       (ds_read_b64_tr_b16), which in each group of 16 lanes gathers four k
+//       rows of 16 values and hands every lane four consecutive k of its own
+//       column; two such reads give the 8 k of an MFMA fragment. The four k
+//       rows of a read then sit in four different bank quarters. fp32
+//       fragments (one k per lane) are plain reads along a row.
+// Rows of at least 128 bytes keep every global request a full cache line:
+// with 64-byte rows the same slab streams measurably slower.
 //
 // Global loads use buffer instructions with a per-operand byte range, so
 // every read past the end of a tensor returns zero: rows past T and the
 // K tail of K = tokens products need no branches. Reads past M or N inside
 // the tensor only feed accumulator rows/columns that the epilogue masks.
 //
-// Pipelining. When both operands are K-contiguous, each K slab goes from
-// global memory straight into LDS (buffer loads with the LDS flag), with as
-// many LDS stages as fit (two for 256 x 256 tiles, three or four for smaller
-// ones): while the MFMAs read stage kt, the slabs of the next NSTAGE-1 steps
-// are in flight, and each step waits only for the oldest. The load
-// instructions of the next slab are interleaved one by one with the MFMAs of
-// the first two k sub-steps, so that a stalled load issue never leaves the
-// matrix cores idle (with one wave per SIMD there is no other wave to fill
-// the gap). Otherwise operands pass through registers (to be transposed)
-// with two LDS stages: during step kt the slab of step kt+1, already in
-// registers, is written to the other stage and the slab of step kt+2 is
-// fetched. MFMA fragments are double-buffered across the 16-wide k
-// sub-steps; one barrier per K step.
+// Pipelining. As many LDS stages as fit (two for 256 x 256 tiles, three or
+// four for smaller ones): while the MFMAs read stage kt, the slabs of the
+// next NSTAGE-1 steps are in flight, and each step waits only for the
+// oldest. The load instructions of the next slab are interleaved one by one
+// with the MFMAs of the first two k sub-steps, so that a stalled load issue
+// never leaves the matrix cores idle (with one wave per SIMD there is no
+// other wave to fill the gap). MFMA fragments are double-buffered across
+// the 16-wide k sub-steps; one barrier per K step.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -159,9 +162,6 @@ struct Cfg {
   static constexpr int NW = WM * WN;
   static constexpr int ES = sizeof(T);
   static constexpr int VEC = 16 / ES;
-  // Operands that are K-contiguous on both sides are loaded straight into
-  // LDS; the others pass through registers.
-  static constexpr bool DIRECT = AKC_ && BKC_;
   static constexpr int RB = kRowBytes;
   static constexpr int CH = RB / 16;  // 16-byte chunks per row
   static constexpr int BK = RB / ES;
@@ -169,11 +169,12 @@ struct Cfg {
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  // The direct path takes as many stages (up to four) as fit next to the
-  // epilogue vectors in the 160 KB of a CU; the register path uses two.
+  // As many stages (up to four) as fit next to the epilogue vectors in the
+  // 160 KB of a CU. A K slab of either layout is 128 bytes of K per tile row
+  // or column.
   static constexpr int VEC_BYTES_ = (BM + BN + WN * BM + WM * BN) * 4;
   static constexpr int FIT_ = (160 * 1024 - VEC_BYTES_) / STAGE_BYTES;
-  static constexpr int NSTAGE = DIRECT ? (FIT_ < 4 ? FIT_ : 4) : 2;
+  static constexpr int NSTAGE = FIT_ < 4 ? FIT_ : 4;
   static_assert(NSTAGE >= 2, "two pipeline stages must fit in LDS");
   static constexpr int PIPE_BYTES = NSTAGE * STAGE_BYTES;
   // Epilogue staging: each wave writes 32 accumulator rows at a time (per
@@ -237,138 +238,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
-
-// ---------------------------------------------------------------------------
-// Operand loader: one K slab (ROWS x BK) of one operand per call.
-// ---------------------------------------------------------------------------
-template <class C, int ROWS, bool KC, bool FROM_TOP, bool ROWSUMSQ>
-struct Loader {
-  static constexpr int VEC = C::VEC;
-  // KC: ROWS*CH chunks; thread t takes chunk t%CH of rows t/CH + u*(NT/CH).
-  static constexpr int CH = C::CH;
-  static constexpr int KC_UNITS = (ROWS * CH) / C::NT;
-  // transposed: (BK/VEC) x (ROWS/VEC) blocks of VEC x VEC elements.
-  static constexpr int BLOCKS = (C::BK / VEC) * (ROWS / VEC);
-  static constexpr int T_UNITS = cdiv(BLOCKS, C::NT);
-  static constexpr int NREG = KC ? KC_UNITS : T_UNITS * VEC;
-  static_assert(!KC || (ROWS * CH) % C::NT == 0, "KC loader: ROWS*CH must divide by NT");
-  static_assert(!KC || KC_UNITS >= 1, "KC loader: too few rows");
-
-  u32x4 r[NREG];
-  float ss[KC ? KC_UNITS : 1];
-
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int u = 0; u < (KC ? KC_UNITS : 1); ++u) ss[u] = 0.f;
-  }
-
-  // Issue the global reads of the slab starting at column/row k0.
-  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int k0, int t) {
-    if constexpr (KC) {
-      const int c = t % CH;
-#pragma unroll
-      for (int u = 0; u < KC_UNITS; ++u) {
-        const int row = t / CH + u * (C::NT / CH);
-        const uint32_t off = (uint32_t)(row * ld_bytes) + (uint32_t)((k0 + c * VEC) * C::ES);
-        r[u] = buf_load16(rs, off);
-      }
-    } else {
-      const int tt = FROM_TOP ? (C::NT - 1 - t) : t;
-#pragma unroll
-      for (int u = 0; u < T_UNITS; ++u) {
-        const int b = u * C::NT + tt;
-        if (BLOCKS % C::NT == 0 || b < BLOCKS) {
-          const int mb = b % (ROWS / VEC), kb = b / (ROWS / VEC);
-#pragma unroll
-          for (int j = 0; j < VEC; ++j) {
-            const int k = k0 + kb * VEC + j;
-            const uint32_t off = (uint32_t)((int64_t)k * ld_bytes) + (uint32_t)(mb * 16);
-            r[u * VEC + j] = buf_load16(rs, off);
-          }
-        }
-      }
-    }
-  }
-
-  // Write the fetched slab into an LDS tile (K-contiguous rows).
-  // `count` says whether this slab lies inside the K range (the pipeline
-  // runs one slab past the end; that slab is never read, and its values must
-  // not enter the row statistics).
-  __device__ __forceinline__ void store(char* tile, int t, bool count = true) {
-    if constexpr (KC) {
-      const int c = t % CH;
-#pragma unroll
-      for (int u = 0; u < KC_UNITS; ++u) {
-        const int row = t / CH + u * (C::NT / CH);
-        *reinterpret_cast<u32x4*>(tile + lds_off(row, c)) = r[u];
-        if constexpr (ROWSUMSQ) {
-          const float add = sumsq16(r[u], 0.f);
-          ss[u] += count ? add : 0.f;
-        }
-      }
-    } else {
-      const int tt = FROM_TOP ? (C::NT - 1 - t) : t;
-#pragma unroll
-      for (int u = 0; u < T_UNITS; ++u) {
-        const int b = u * C::NT + tt;
-        if (BLOCKS % C::NT == 0 || b < BLOCKS) {
-          const int mb = b % (ROWS / VEC), kb = b / (ROWS / VEC);
-          u32x4 o[VEC];
-          transpose(&r[u * VEC], o);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i)
-            *reinterpret_cast<u32x4*>(tile + lds_off(mb * VEC + i, kb)) = o[i];
-        }
-      }
-    }
-  }
-
-  // Sum of squares of the 16 bytes of one chunk, accumulated into acc.
-  static __device__ __forceinline__ float sumsq16(u32x4 v, float acc) {
-    if constexpr (C::ES == 2) {
-      // The words are copied to scalars first: bit-casting a vector element
-      // selected by the loop index straight into the dot2 builtin makes this
-      // compiler read word 0 four times.
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const bf16x2 p = __builtin_bit_cast(bf16x2, wv[w]);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = __uint_as_float(v[w]);
-        acc = __builtin_fmaf(f, f, acc);
-      }
-    }
-    return acc;
-  }
-
-  // in[j] holds VEC elements (m = 0..VEC-1) of K row j; out[i] gets the VEC
-  // K values of m = i.
-  static __device__ __forceinline__ void transpose(const u32x4* in, u32x4* out) {
-    if constexpr (C::ES == 2) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t x = in[2 * p][i >> 1], y = in[2 * p + 1][i >> 1];
-          out[i][p] = (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) out[i][p] = in[p][i];
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
 // Direct-to-LDS loader for a K-contiguous operand. One buffer_load_dwordx4
 // with the LDS flag writes 64 lanes x 16 bytes to LDS at a wave-uniform base
@@ -399,6 +268,77 @@ struct DirectLoader {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS loader for an M- (or N-) contiguous operand: a K slab is BK
+// rows of k, each COLS values (RS bytes) wide. One instruction fills 1024
+// contiguous LDS bytes, i.e. 1024/RS k rows; lane l writes slot l % CHR of
+// row l / CHR and fetches the chunk that the swizzle of that row places
+// there.
+// ---------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ int mn_swz(int k) {
+  if constexpr (C::ES == 2) return 4 * (k & 3);
+  else return 8 * (k & 1);
+}
+
+template <class C, int COLS>
+struct DirectLoaderMN {
+  static constexpr int RS = COLS * C::ES;  // LDS bytes per k row
+  static constexpr int CHR = RS / 16;      // chunks per row
+  static constexpr int RPI = 1024 / RS;    // k rows per instruction
+  static constexpr int INSTR = C::BK / RPI / C::NW;
+  static_assert(CHR >= 16 && 1024 % RS == 0, "MN tile rows must be 256 to 1024 bytes");
+  static_assert(C::BK % (RPI * C::NW) == 0, "direct loader: rows must split evenly over the waves");
+  // k0: first k row of the slab (relative to the operand base); oob as for
+  // the K-contiguous loader.
+  __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int k0, char* tile,
+                                               int wave, int lane, uint32_t oob = 0) {
+#pragma unroll
+    for (int q = 0; q < INSTR; ++q) {
+      const int row0 = RPI * (q * C::NW + wave);
+      const int row = row0 + lane / CHR;
+      const int chunk = (lane % CHR) ^ mn_swz<C>(row);
+      const uint32_t off = ((uint32_t)((k0 + row) * ld_bytes) + (uint32_t)(chunk * 16)) | oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + row0 * RS), 16, off, 0, 0, 0);
+    }
+  }
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// MFMA fragment of an operand stored MN-major in LDS (RS bytes per k row):
+// lane l gets the KL values k = k0 + KL*(l/32) + 0..KL-1 of column
+// c0 + l%32 (c0 = first column of the 32-wide fragment block).
+template <class C, int RS>
+struct MnFrag {
+  typedef typename Mfma<typename C::T>::Frag Frag;
+  __device__ __forceinline__ static Frag read(const char* tile, int c0, int k0, int lane) {
+    if constexpr (C::ES == 2) {
+      // ds_read_b64_tr_b16: in each group g of 16 lanes, source lane j reads
+      // 4 consecutive columns at one k row, and lane i receives component
+      // (i & 3) of source lanes 4e + (i >> 2), e = 0..3. Source lane j of
+      // group g therefore points at k row k0 + 8 (g >> 1) + (j >> 2) (+4 for
+      // the second read) and columns c0 + 16 (g & 1) + 4 (j & 3).
+      const int g = lane >> 4, j = lane & 15;
+      const int col = c0 + 16 * (g & 1) + 4 * (j & 3);  // 4 columns = 8 bytes
+      const int chunk = col >> 3, half = (col >> 2) & 1;
+      const int k = k0 + 8 * (g >> 1) + (j >> 2);
+      const int a0 = k * RS + ((chunk ^ mn_swz<C>(k)) << 4) + 8 * half;
+      const int a1 = (k + 4) * RS + ((chunk ^ mn_swz<C>(k + 4)) << 4) + 8 * half;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + a0));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + a1));
+      const v8i16 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(Frag, w);
+    } else {
+      const int k = k0 + (lane >> 5), col = c0 + (lane & 31);
+      return *reinterpret_cast<const float*>(tile + k * RS + ((((col * 4) >> 4) ^ mn_swz<C>(k)) << 4) +
+                                             ((col * 4) & 15));
+    }
+  }
+};
+
 // s_waitcnt vmcnt(n) with the other counters unconstrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -406,10 +346,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Load instructions a K step interleaves with the MFMAs of sub-steps 0 and 1.
-template <int V0, int V1>
+// Where a K step issues the next slab's loads: VA instructions for A in
+// sub-step PA and VB for B in sub-step PB, each interleaved with the MFMAs
+// of its sub-step.
+template <int VA, int PA, int VB, int PB>
 struct SlabPlan {
-  static constexpr int at(int kk) { return kk == 0 ? V0 : (kk == 1 ? V1 : 0); }
+  static constexpr int A_AT = PA, B_AT = PB;
+  static constexpr int at(int kk) { return (kk == PA ? VA : 0) + (kk == PB ? VB : 0); }
 };
 
 // ---------------------------------------------------------------------------
@@ -550,6 +493,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool RSS = E::kRowSumsq;
   static_assert(!RSS || C::NACC == 1, "row statistics are taken in single-accumulator products");
+  static_assert(!RSS || C::AKC, "row statistics are taken from K-contiguous A fragments");
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -576,8 +520,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[p][i][j][v] = 0.f;
 
-  Loader<C, C::BM, C::AKC, false, false> la;
-  Loader<C, C::BN, C::BKC, true, false> lb;
   constexpr int KK = C::BK / MF::KI;
   // Online-RMSNorm statistic: sums of squares of the A rows, taken from the
   // MFMA A fragments (each lane holds 8 k-values of one row per sub-step).
@@ -600,24 +542,36 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
     const int64_t lda_b = A.ld * C::ES, ldb_b = B.ld * C::ES;
     const int kl = (lane >> 5) * MF::KL;
 
-    // MFMAs of one LDS stage. With NV = 0, `stage_work(kk)` runs after
-    // sub-step kk's MFMAs have been issued (staging of the register path).
-    // With NV > 0, stage_work(kk) issues NV(kk) global->LDS load
-    // instructions (the first two sub-steps), which are interleaved one by
-    // one with that sub-step's MFMAs.
+    // Loaders and fragment readers of this operand layout pair.
+    typedef std::conditional_t<C::AKC, DirectLoader<C, C::BM>, DirectLoaderMN<C, C::BM>> DA;
+    typedef std::conditional_t<C::BKC, DirectLoader<C, C::BN>, DirectLoaderMN<C, C::BN>> DB;
+    auto frag_a = [&](const char* As, int i, int k) {
+      if constexpr (C::AKC) return MF::read(As, wm * C::WTM + i * 32 + (lane & 31), k + kl);
+      else return MnFrag<C, C::BM * C::ES>::read(As, wm * C::WTM + i * 32, k, lane);
+    };
+    auto frag_b = [&](const char* Bs, int j, int k) {
+      if constexpr (C::BKC) return MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), k + kl);
+      else return MnFrag<C, C::BN * C::ES>::read(Bs, wn * C::WTN + j * 32, k, lane);
+    };
+
+    // MFMAs of one LDS stage. stage_work(kk) issues the NV(kk) global->LDS
+    // load instructions of a later slab (sub-steps 0 and 1), interleaved one
+    // by one with that sub-step's MFMAs.
     auto compute = [&](const char* As, const char* Bs, auto nv_tag, auto&& stage_work) {
       typedef decltype(nv_tag) NV;
       typename MF::Frag fa[2][C::FM], fb[2][C::FN];
-      static_for<0, C::FM>([&](auto i) { fa[0][i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), kl); });
-      static_for<0, C::FN>([&](auto j) { fb[0][j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), kl); });
-      __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);  // sub-step 0's reads lead
+      static_for<0, C::FM>([&](auto i) { fa[0][i] = frag_a(As, i, 0); });
+      static_for<0, C::FN>([&](auto j) { fb[0][j] = frag_b(Bs, j, 0); });
+      // LDS read instructions per sub-step (a bf16 MN-major fragment takes two)
+      constexpr int NR = C::FM * (C::AKC || C::ES == 4 ? 1 : 2) + C::FN * (C::BKC || C::ES == 4 ? 1 : 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // sub-step 0's reads lead
       static_for<0, KK>([&](auto kk) {
         constexpr int cur = kk & 1, nxt = cur ^ 1;
         constexpr int nv = NV::at(kk);
         if constexpr (kk + 1 < KK) {
-          const int k = (kk + 1) * MF::KI + kl;
-          static_for<0, C::FM>([&](auto i) { fa[nxt][i] = MF::read(As, wm * C::WTM + i * 32 + (lane & 31), k); });
-          static_for<0, C::FN>([&](auto j) { fb[nxt][j] = MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), k); });
+          const int k = (kk + 1) * MF::KI;
+          static_for<0, C::FM>([&](auto i) { fa[nxt][i] = frag_a(As, i, k); });
+          static_for<0, C::FN>([&](auto j) { fb[nxt][j] = frag_b(Bs, j, k); });
         }
         static_for<0, C::FM>([&](auto i) {
           static_for<0, C::FN>([&](auto j) { acc[p][i][j] = MF::mma(fa[cur][i], fb[cur][j], acc[p][i][j]); });
@@ -627,7 +581,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
         // sub-step kk (with the slab loads, if any, one after every few
         // MFMAs), so the reads have a whole sub-step of MFMAs to land (left
         // alone, the scheduler issues each read just before its use).
-        if constexpr (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);
+        if constexpr (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
         if constexpr (nv > 0) {
           constexpr int NM = C::FM * C::FN;
           static_for<0, nv>([&](auto v) {
@@ -639,85 +593,55 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
           __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
         }
         if constexpr (RSS) static_for<0, C::FM>([&](auto i) { ss[i] = frag_sumsq(fa[cur][i], ss[i]); });
-        if constexpr (nv == 0) stage_work(kk);
       });
     };
 
-    if constexpr (C::DIRECT) {
-      typedef DirectLoader<C, C::BM> DA;
-      typedef DirectLoader<C, C::BN> DB;
-      constexpr int L = DA::INSTR + DB::INSTR;  // loads per wave per K slab
-      constexpr int NS = C::NSTAGE;
-      // Every step issues exactly one slab (past the end of K, out of range),
-      // so L * (NS-2) loads still outstanding means slab kt has landed.
-      static_for<0, NS - 1>([&](auto s) {
-        const uint32_t oob = s() < KT ? 0u : 0x80000000u;
-        char* st = smem + s() * C::STAGE_BYTES;
-        DA::issue(ra, lda_b, kbeg + s() * C::BK, st, wave, lane, oob);
-        DB::issue(rb, ldb_b, kbeg + s() * C::BK, st + C::A_BYTES, wave, lane, oob);
+    constexpr int L = DA::INSTR + DB::INSTR;  // loads per wave per K slab
+    // The compiler cannot tell the transposing LDS reads apart from the
+    // slab being loaded into another stage, and waits for every load in
+    // flight before each of them. With an MN-major operand the next slab is
+    // therefore issued in the last sub-step, after the stage's last reads.
+    typedef std::conditional_t<C::AKC && C::BKC, SlabPlan<DA::INSTR, 0, DB::INSTR, 1>,
+                               SlabPlan<DA::INSTR, KK - 1, DB::INSTR, KK - 1>> Plan;
+    constexpr int NS = C::NSTAGE;
+    // Every step issues exactly one slab (past the end of K, out of range),
+    // so L * (NS-2) loads still outstanding means slab kt has landed.
+    static_for<0, NS - 1>([&](auto s) {
+      const uint32_t oob = s() < KT ? 0u : 0x80000000u;
+      char* st = smem + s() * C::STAGE_BYTES;
+      DA::issue(ra, lda_b, kbeg + s() * C::BK, st, wave, lane, oob);
+      DB::issue(rb, ldb_b, kbeg + s() * C::BK, st + C::A_BYTES, wave, lane, oob);
+    });
+    int cur = 0;       // stage read in this step
+    int nxt = NS - 1;  // stage refilled in this step
+    for (int kt = 0; kt < KT; ++kt) {
+      // Slabs kt .. kt+NS-2 are in flight; wait for slab kt only.
+      wait_vmcnt<L * (NS - 2)>();
+      // A plain s_barrier: __syncthreads() would add a release fence that
+      // waits for every outstanding load, including the slabs still allowed
+      // in flight. The empty asm statements keep the compiler from moving
+      // LDS accesses across the barrier.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // Slab kt+NS-1 goes to the stage last read in step kt-1, which every
+      // wave has finished once past the barrier. Past the end of K the loads
+      // are issued out of range and fetch nothing.
+      const int ks = kt + NS - 1;
+      const uint32_t oob = ks < KT ? 0u : 0x80000000u;
+      char* st = smem + nxt * C::STAGE_BYTES;
+      const char* As = smem + cur * C::STAGE_BYTES;
+      compute(As, As + C::A_BYTES, Plan{}, [&](auto kk) {
+        if constexpr (kk == Plan::A_AT) DA::issue(ra, lda_b, kbeg + ks * C::BK, st, wave, lane, oob);
+        if constexpr (kk == Plan::B_AT) DB::issue(rb, ldb_b, kbeg + ks * C::BK, st + C::A_BYTES, wave, lane, oob);
       });
-      int cur = 0;       // stage read in this step
-      int nxt = NS - 1;  // stage refilled in this step
-      for (int kt = 0; kt < KT; ++kt) {
-        // Slabs kt .. kt+NS-2 are in flight; wait for slab kt only.
-        wait_vmcnt<L * (NS - 2)>();
-        // A plain s_barrier: __syncthreads() would add a release fence that
-        // waits for every outstanding load, including the slabs still
-        // allowed in flight. The empty asm statements keep the compiler from
-        // moving LDS accesses across the barrier.
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        // Slab kt+NS-1 goes to the stage last read in step kt-1, which every
-        // wave has finished once past the barrier. Past the end of K the
-        // loads are issued out of range and fetch nothing.
-        const int ks = kt + NS - 1;
-        const uint32_t oob = ks < KT ? 0u : 0x80000000u;
-        char* st = smem + nxt * C::STAGE_BYTES;
-        const char* As = smem + cur * C::STAGE_BYTES;
-        compute(As, As + C::A_BYTES, SlabPlan<DA::INSTR, DB::INSTR>{}, [&](auto kk) {
-          if constexpr (kk == 0) DA::issue(ra, lda_b, kbeg + ks * C::BK, st, wave, lane, oob);
-          if constexpr (kk == 1) DB::issue(rb, ldb_b, kbeg + ks * C::BK, st + C::A_BYTES, wave, lane, oob);
-        });
-        cur = cur + 1 == NS ? 0 : cur + 1;
-        nxt = nxt + 1 == NS ? 0 : nxt + 1;
-      }
-      // Out-of-range loads still count; none may land after the epilogue
-      // starts reusing this LDS.
-      wait_vmcnt<0>();
-      __syncthreads();
-    } else {
-      la.fetch(ra, lda_b, kbeg, t);
-      lb.fetch(rb, ldb_b, kbeg, t);
-      la.store(smem, t);
-      lb.store(smem + C::A_BYTES, t);
-      la.fetch(ra, lda_b, kbeg + C::BK, t);
-      lb.fetch(rb, ldb_b, kbeg + C::BK, t);
-      for (int kt = 0; kt < KT; ++kt) {
-        __syncthreads();
-        const char* As = smem + (kt & 1) * C::STAGE_BYTES;
-        char* Ns = smem + ((kt & 1) ^ 1) * C::STAGE_BYTES;
-        // Staging work after the first two sub-steps' MFMAs have been issued:
-        // each operand's slab for step kt+1 goes to the other LDS stage and
-        // its registers are refilled at once with step kt+2, so every global
-        // load has a whole K step to land. The scheduling barriers keep the
-        // compiler from sinking the loads to the end of the step.
-        compute(As, As + C::A_BYTES, SlabPlan<0, 0>{}, [&](auto kk) {
-          if constexpr (kk == 0 || kk == 1) {
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (kk == 0) {
-              la.store(Ns, t);
-              la.fetch(ra, lda_b, kbeg + (kt + 2) * C::BK, t);
-            } else {
-              lb.store(Ns + C::A_BYTES, t);
-              lb.fetch(rb, ldb_b, kbeg + (kt + 2) * C::BK, t);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        });
-      }
-      __syncthreads();
+      cur = cur + 1 == NS ? 0 : cur + 1;
+      nxt = nxt + 1 == NS ? 0 : nxt + 1;
     }
+    // Out-of-range loads still count; none may land after the epilogue
+    // starts reusing this LDS (or the next accumulator's prologue refills it).
+    wait_vmcnt<0>();
+    __syncthreads();
   });
 
   float* rowv = reinterpret_cast<float*>(smem + C::SCR_BYTES);
