@@ -83,9 +83,11 @@ struct CfgInfo {
 };
 constexpr CfgInfo kCfg[] = {{256, 256, 1.00}, {256, 128, 0.88}, {128, 128, 0.70}, {64, 64, 1.0}};
 
-template <bool AKC, bool BKC, int NACC> using C256 = Cfg<bf16, 256, 256, 2, 2, AKC, BKC, NACC>;
-template <bool AKC, bool BKC, int NACC> using C256x128 = Cfg<bf16, 256, 128, 2, 2, AKC, BKC, NACC>;
-template <bool AKC, bool BKC, int NACC> using C128 = Cfg<bf16, 128, 128, 2, 2, AKC, BKC, NACC>;
+// bf16 tiles run 8 waves (two per SIMD): while one wave waits on a barrier,
+// an LDS read or a load issue, the other keeps the matrix core busy.
+template <bool AKC, bool BKC, int NACC> using C256 = Cfg<bf16, 256, 256, 2, 4, AKC, BKC, NACC>;
+template <bool AKC, bool BKC, int NACC> using C256x128 = Cfg<bf16, 256, 128, 4, 2, AKC, BKC, NACC>;
+template <bool AKC, bool BKC, int NACC> using C128 = Cfg<bf16, 128, 128, 2, 4, AKC, BKC, NACC>;
 template <bool AKC, bool BKC, int NACC> using CF32 = Cfg<float, 64, 64, 2, 2, AKC, BKC, NACC>;
 
 struct Choice {
