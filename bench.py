@@ -300,6 +300,90 @@ def cpu_baseline(name, target_s):
             "tokens_per_s": Ts / dt}
 
 
+
+# ---------------------------------------------------------------------------
+# rocprofv3 post-processing (CSV output of --kernel-trace --stats and --pmc)
+# ---------------------------------------------------------------------------
+
+# Kernels of the MLP step whose instantiation (epilogue type) is unique, so a
+# rocprofv3 kernel name identifies the launch label.
+MLP_LABEL_PATTERNS = {
+    "mlp_recompute_swiglu_bwd": "NS_12EpiSwigluBwd",
+    "mlp_up1_swiglu": "NS_9EpiSwigluE",
+    "mlp_down1": "NS_7EpiDownILb1",
+    "mlp_down2": "NS_7EpiDownILb0",
+    "mlp1_dx": "NS_5EpiDXE",
+    "mlp1_ds": "NS_5EpiDSILb1",
+    "mlp_ds2": "NS_5EpiDSILb0",
+}
+
+
+def short_kernel_name(n: str) -> str:
+    import re
+    m = re.search(r"CfgI(DF16b|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELb(\d)ELb(\d)ELi(\d)EEENS_(\d+)(\w+?)(ILb(\d)EE)?EEE", n)
+    if m:
+        t = "bf16" if m.group(1) == "DF16b" else "f32"
+        lay = ("KC" if m.group(6) == "1" else "MC") + "/" + ("KC" if m.group(7) == "1" else "NC")
+        epi = m.group(10) + (f"<{m.group(12)}>" if m.group(12) else "")
+        return f"gemm {t} {m.group(2)}x{m.group(3)} waves {m.group(4)}x{m.group(5)} {lay} nacc={m.group(8)} {epi}"
+    return n.split("(")[0].replace("void ", "")
+
+
+def summarize_stats(csv_path: str, title: str, command: str) -> str:
+    """Markdown table from a rocprofv3 kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+           "| kernel | calls | avg (us) | min (us) | max (us) | total (us) | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def counter_per_kernel(csv_path: str, counter: str):
+    """{kernel name: [per-dispatch values]} of one counter from counter_collection.csv."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def traffic_json(fetch_csv: str, write_csv: str, workload: str, copy_mib: int) -> dict:
+    """Per-launch HBM bytes of the labelled kernels, each counter scaled by the
+    factor that makes the calibration copy (copy_mib MiB read and written by
+    one blit kernel) read exactly its size."""
+    fetch = counter_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = counter_per_kernel(write_csv, "WRITE_SIZE")
+    known = float(copy_mib << 20)
+
+    def copy_kib(per):
+        vals = [max(v) for k, v in per.items() if "copyBuffer" in k or "copy" in k.lower()]
+        return max(vals) if vals else None
+
+    fk, wk = copy_kib(fetch), copy_kib(write)
+    if not fk or not wk:
+        raise SystemExit("no calibration copy kernel in the counter files")
+    f_scale, w_scale = known / (fk * 1024.0), known / (wk * 1024.0)
+    kernels = {}
+    for label, pat in MLP_LABEL_PATTERNS.items():
+        fn = [k for k in fetch if pat in k]
+        wn = [k for k in write if pat in k]
+        if len(fn) != 1 or len(wn) != 1:
+            continue
+        fv, wv = fetch[fn[0]], write[wn[0]]
+        kernels[label] = {"kernel": short_kernel_name(fn[0]), "dispatches": len(fv),
+                          "fetch_bytes": round(sum(fv) / len(fv) * 1024.0 * f_scale),
+                          "write_bytes": round(sum(wv) / len(wv) * 1024.0 * w_scale)}
+    return {"source_digest": source_digest(), "workload": workload,
+            "calibration": {"copy_bytes": int(known), "fetch_kib_read": fk, "write_kib_read": wk,
+                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+            "kernels": kernels}
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -314,7 +398,21 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before timing, copy this many MiB once with a plain device copy, so that a "
                          "counter profile of this run holds a copy kernel of known traffic")
+    ap.add_argument("--summarize-stats", metavar="CSV", help="print a markdown summary of a rocprofv3 "
+                    "kernel_stats.csv (with --title, --command) and exit")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the per-launch HBM traffic JSON from two rocprofv3 --pmc counter_collection.csv "
+                         "files (FETCH_SIZE, WRITE_SIZE; runs made with --calibrate-copy-mib) and exit")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="")
     args = ap.parse_args()
+    if args.summarize_stats:
+        sys.stdout.write(summarize_stats(args.summarize_stats, args.title, args.command))
+        return
+    if args.traffic:
+        print(json.dumps(traffic_json(args.traffic[0], args.traffic[1], args.workload,
+                                      args.calibrate_copy_mib or 1024), indent=1))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
