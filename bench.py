@@ -82,6 +82,9 @@ def lrblock_kernel_flops(T, d, r, G, n, bwd=True):
     return f
 
 
+RECOMPUTE_LABELS = ("mlp_recompute_swiglu_bwd", "btp_u_bwd")
+
+
 def btp_kernel_flops(T, r, ds):
     return {"btp_u": 2 * T * r * ds, "btp_p": 2 * T * ds * r, "btp_e": 2 * T * r * ds,
             "btp_u_bwd": 2 * T * r * ds, "btp_dA": 2 * ds * r * T, "btp_dB": 2 * r * ds * T,
@@ -125,11 +128,13 @@ class Workload:
             bo = B.lrmlp_bwd(t["x"], t["g"], t["A1_cat"], t["B1"], t["A2"], t["B2"], *fo[1:], t["dY"], ws=ws_b)
             args = [t[k] for k in ("x", "g", "A1_cat", "B1", "A2", "B2")]
 
-            def step():
+            def fwd():
                 B.lrmlp_fwd(*args, out=fo, ws=ws_f)
+
+            def bwd():
                 B.lrmlp_bwd(*args, *fo[1:], t["dY"], out=bo, ws=ws_b)
 
-            self.step = step
+            self.fwd, self.bwd_fn = fwd, bwd
             self.tokens = T
             self.kflops = mlp_kernel_flops(T, d, r, ffn)
             self.shape = dict(T=T, d=d, r=r, ffn=ffn)
@@ -144,12 +149,13 @@ class Workload:
             bo = B.lrblock_bwd(t["x"], t["g"], t["A_cat"], t["B"], fo[1], fo[2], t["dY"], ws=ws_b) \
                 if self.bwd else None
 
-            def step():
+            def fwd():
                 B.lrblock_fwd(t["x"], t["g"], t["A_cat"], t["B"], out=fo, ws=ws_f)
-                if self.bwd:
-                    B.lrblock_bwd(t["x"], t["g"], t["A_cat"], t["B"], fo[1], fo[2], t["dY"], out=bo, ws=ws_b)
 
-            self.step = step
+            def bwd():
+                B.lrblock_bwd(t["x"], t["g"], t["A_cat"], t["B"], fo[1], fo[2], t["dY"], out=bo, ws=ws_b)
+
+            self.fwd, self.bwd_fn = fwd, (bwd if self.bwd else None)
             self.tokens = T
             self.kflops = lrblock_kernel_flops(T, d, r, G, n, self.bwd)
             self.shape = dict(T=T, d=d, r=r, G=G, d_out=n)
@@ -166,11 +172,13 @@ class Workload:
             fo = B.btp_share_fwd(*args, ws=ws_f)
             bo = B.btp_share_bwd(*args, t["dp"], ds, ws=ws_b)
 
-            def step():
+            def fwd():
                 B.btp_share_fwd(*args, out=fo, ws=ws_f)
+
+            def bwd():
                 B.btp_share_bwd(*args, t["dp"], ds, out=bo, ws=ws_b)
 
-            self.step = step
+            self.fwd, self.bwd_fn = fwd, bwd
             self.tokens = T
             self.kflops = btp_kernel_flops(T, r, D // P)
             self.shape = dict(T=T, r=r, d_shard=D // P, d_global=D, tp=P)
@@ -200,38 +208,54 @@ class Workload:
                 state[act] = (qf, qb, of, ob, mf, mb)
             self.act = self.acts[0]
 
-            def step():
+            ma = [m[k] for k in ("x", "g", "A1_cat", "B1", "A2", "B2")]
+
+            def fwd():
                 act = self.act
                 qf, qb, of, ob, mf, mb = state[act]
-                ma = [m[k] for k in ("x", "g", "A1_cat", "B1", "A2", "B2")]
                 B.lrblock_fwd(q["x"], q["g"], q["A_cat"], q["B"], act=act, out=qf, ws=ws)
-                B.lrblock_bwd(q["x"], q["g"], q["A_cat"], q["B"], qf[1], qf[2], q["dY"], act=act, out=qb, ws=ws)
                 B.lrblock_fwd(o["x"], None, o["A_cat"], o["B"], act=act, norm=False, out=of, ws=ws)
+                B.lrmlp_fwd(*ma, act=act, out=mf, ws=ws)
+
+            def bwd():
+                act = self.act
+                qf, qb, of, ob, mf, mb = state[act]
+                B.lrblock_bwd(q["x"], q["g"], q["A_cat"], q["B"], qf[1], qf[2], q["dY"], act=act, out=qb, ws=ws)
                 B.lrblock_bwd(o["x"], None, o["A_cat"], o["B"], of[1], None, o["dY"], act=act, norm=False,
                               out=ob, ws=ws)
-                B.lrmlp_fwd(*ma, act=act, out=mf, ws=ws)
                 B.lrmlp_bwd(*ma, *mf[1:], m["dY"], act=act, out=mb, ws=ws)
 
-            self.step = step
+            self.fwd, self.bwd_fn = fwd, bwd
             self.tokens = T
             # QKV and O launches share the lrblock_* labels with different
             # per-launch flops, so only the MLP kernels get a roofline here.
             self.kflops = mlp_kernel_flops(T, d, r, ffn)
             self.shape = dict(T=T, d=d, r=r, ffn=ffn)
         self.flops = self.step_flops()
+        self.model_flops = self.step_flops(model_only=True)
 
-    def step_flops(self) -> float:
+    def step(self):
+        self.fwd()
+        if self.bwd_fn is not None:
+            self.bwd_fn()
+
+    def step_flops(self, model_only: bool = False) -> float:
+        """Algorithmic flops of one step; model_only drops the prescribed
+        recompute (the gate/up re-forward of the MLP, u of the BTP share)."""
         w = self.w
+
+        def tot(f):
+            return float(sum(v for k, v in f.items() if not (model_only and k in RECOMPUTE_LABELS)))
+
         if self.kind == "lrmlp":
-            return float(sum(mlp_kernel_flops(w["T"], w["d"], w["r"], w["ffn"]).values()))
+            return tot(mlp_kernel_flops(w["T"], w["d"], w["r"], w["ffn"]))
         if self.kind == "lrblock":
-            return float(sum(lrblock_kernel_flops(w["T"], w["d"], w["r"], w["G"], w["d_out"], self.bwd).values()))
+            return tot(lrblock_kernel_flops(w["T"], w["d"], w["r"], w["G"], w["d_out"], self.bwd))
         if self.kind == "btp":
-            return float(sum(btp_kernel_flops(w["T"], w["r"], w["d_global"] // w["P"]).values()))
+            return tot(btp_kernel_flops(w["T"], w["r"], w["d_global"] // w["P"]))
         T, d, r, ffn = w["T"], w["d"], w["r"], w["ffn"]
-        return float(sum(lrblock_kernel_flops(T, d, r, 3, d).values()) +
-                     sum(lrblock_kernel_flops(T, d, r, 1, d).values()) +
-                     sum(mlp_kernel_flops(T, d, r, ffn).values()))
+        return (tot(lrblock_kernel_flops(T, d, r, 3, d)) + tot(lrblock_kernel_flops(T, d, r, 1, d)) +
+                tot(mlp_kernel_flops(T, d, r, ffn)))
 
 
 # ---------------------------------------------------------------------------
@@ -294,7 +318,20 @@ def cpu_baseline(name, target_s):
     Ts = int(min(T, max(probe, probe * target_s / max(dt, 1e-3))))
     Ts = max(64, Ts // 64 * 64) if T >= 64 else T
     dt, fl = run(Ts)
+    cpu_model, blas = "unknown", "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"]
+    except Exception:
+        pass
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": f"fp64 NumPy oracle, fwd+bwd of the first {Ts} of {T} tokens of the same workload "
                       f"(algorithmic flops scaled to the sample), {dt:.1f} s",
             "tokens_per_s": Ts / dt}
@@ -353,6 +390,28 @@ def counter_per_kernel(csv_path: str, counter: str):
     return per
 
 
+def mfma_summary(csv_path: str, title: str, command: str) -> str:
+    """Markdown table of MFMA utilisation (rocprofv3 derived counter MfmaUtil)
+    and hardware-counted bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
+    per labelled kernel of the MLP step, against its algorithmic flops."""
+    util = counter_per_kernel(csv_path, "MfmaUtil")
+    mops = counter_per_kernel(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    kf = mlp_kernel_flops(**{k: synth.WORKLOADS["llama2_7b_mlp"][k] for k in ("T", "d", "r", "ffn")})
+    out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+           "| launch | kernel | MFMA busy (% of SIMD cycles) | counted MFMA GF | algorithmic GF | counted / algorithmic |",
+           "|---|---|---|---|---|---|"]
+    for label, pat in MLP_LABEL_PATTERNS.items():
+        un = [k for k in util if pat in k]
+        mn = [k for k in mops if pat in k]
+        if len(un) != 1 or len(mn) != 1:
+            continue
+        u = sum(util[un[0]]) / len(util[un[0]])
+        gf = sum(mops[mn[0]]) / len(mops[mn[0]]) * 512 / 1e9
+        out.append(f"| {label} | {short_kernel_name(un[0])} | {u:.1f} | {gf:.1f} | {kf[label] / 1e9:.1f} | "
+                   f"{gf * 1e9 / kf[label]:.3f} |")
+    return "\n".join(out) + "\n"
+
+
 def traffic_json(fetch_csv: str, write_csv: str, workload: str, copy_mib: int) -> dict:
     """Per-launch HBM bytes of the labelled kernels, each counter scaled by the
     factor that makes the calibration copy (copy_mib MiB read and written by
@@ -395,6 +454,8 @@ def main():
     ap.add_argument("--act", default=None, help="bottleneck activation for the layer set (silu|identity)")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--flush-steps", type=int, default=5,
+                    help="steps of a second, untimed-for-value pass with the last-level cache flushed before each")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before timing, copy this many MiB once with a plain device copy, so that a "
                          "counter profile of this run holds a copy kernel of known traffic")
@@ -403,11 +464,17 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the per-launch HBM traffic JSON from two rocprofv3 --pmc counter_collection.csv "
                          "files (FETCH_SIZE, WRITE_SIZE; runs made with --calibrate-copy-mib) and exit")
+    ap.add_argument("--mfma-summary", metavar="CSV", help="print MFMA utilisation per kernel from a rocprofv3 "
+                    "--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 counter_collection.csv (with --title, --command) "
+                    "and exit")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.summarize_stats:
         sys.stdout.write(summarize_stats(args.summarize_stats, args.title, args.command))
+        return
+    if args.mfma_summary:
+        sys.stdout.write(mfma_summary(args.mfma_summary, args.title, args.command))
         return
     if args.traffic:
         print(json.dumps(traffic_json(args.traffic[0], args.traffic[1], args.workload,
@@ -456,21 +523,47 @@ def main():
     log("kernel times in one step (ms):", json.dumps({k: round(v, 4) for k, v in
                                                        sorted(per_kernel.items(), key=lambda kv: -kv[1])}))
 
-    # Timed region: K steps, HIP events around the dominant kernel's launches.
+    # Timed region: K steps, HIP events around the dominant kernel's launches
+    # and at every forward/backward boundary (fwd and bwd split, median, min).
     B.profiler_enable(dom, 64 * max(1, args.steps))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        wl.step()
-    e1.record(stream)
+    ev[0].record(stream)
+    for i in range(args.steps):
+        wl.fwd()
+        ev[2 * i + 1].record(stream)
+        if wl.bwd_fn is not None:
+            wl.bwd_fn()
+        ev[2 * i + 2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[2 * args.steps]) / args.steps
+    fwd_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
+    bwd_ms = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)]
+    step_ms = [a + b for a, b in zip(fwd_ms, bwd_ms)]
     rep = B.profiler_report()
     B.profiler_disable()
+
+    # Second pass, not part of `value`: the 256 MB last-level cache is flushed
+    # (a 512 MB buffer is written) before every step, so inputs come from HBM.
+    flushed = None
+    if args.flush_steps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        fl = []
+        for i in range(args.flush_steps):
+            scratch.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            wl.step()
+            b.record(stream)
+            fl.append((a, b))
+        torch.cuda.synchronize()
+        fms = sorted(a.elapsed_time(b) for a, b in fl)
+        flushed = {"steps": args.flush_steps, "ms_median": round(fms[len(fms) // 2], 4), "ms_min": round(fms[0], 4),
+                   "tflops_median": round(wl.flops / (fms[len(fms) // 2] * 1e-3) / 1e12, 2)}
+        del scratch
 
     cnt, tot = rep.get(dom, (0, 0.0))
     avg_ms = tot / max(cnt, 1)
@@ -493,11 +586,24 @@ def main():
                     "kernel_avg_ms": round(avg_ms, 5), "launches_per_step": launches_per_step,
                     "algorithmic_gflop_per_launch": round(dom_flops / 1e9, 3)}
 
+    def med(v):
+        return sorted(v)[len(v) // 2]
+
+    kernels = {}
+    for k, kms in sorted(per_kernel.items(), key=lambda kv: -kv[1]):
+        kf = wl.kflops.get(k)
+        kernels[k] = {"ms": round(kms, 4)}
+        if kf and kms > 0:
+            kernels[k]["tflops"] = round(kf / (kms * 1e-3) / 1e12, 1)
+            kernels[k]["frac"] = round(kf / (kms * 1e-3) / 1e12 / peak, 4)
+
     cpu = None
     if args.cpu_baseline == "on":
         log("timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(args.workload, args.cpu_seconds)
 
+    if cpu:
+        cpu["gpu_over_cpu"] = round(value / cpu["value"], 1)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -518,6 +624,14 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "timing": {"step_ms_median": round(med(step_ms), 4), "step_ms_min": round(min(step_ms), 4),
+                   "fwd_ms_median": round(med(fwd_ms), 4), "fwd_ms_min": round(min(fwd_ms), 4),
+                   "bwd_ms_median": round(med(bwd_ms), 4) if wl.bwd_fn else None,
+                   "bwd_ms_min": round(min(bwd_ms), 4) if wl.bwd_fn else None,
+                   "model_only_tflops": round(wl.model_flops / (ms * 1e-3) / 1e12, 2),
+                   "model_only_gflop_per_step": round(wl.model_flops / 1e9, 2),
+                   "mall_flushed": flushed},
+        "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
 
