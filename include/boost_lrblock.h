@@ -37,7 +37,13 @@
  *   - Ownership: the caller owns every buffer. The library allocates no
  *     device memory, frees nothing, keeps no pointer after return and never
  *     synchronises. Work is enqueued on `stream` (a hipStream_t; NULL = the
- *     default stream) in stream order and runs asynchronously.
+ *     default stream) in stream order and runs asynchronously. The backward
+ *     calls fork their weight-gradient products onto a side stream (one per
+ *     host thread and device, created on first use with the default
+ *     priority) through an event recorded on `stream`, and make `stream`
+ *     wait for them before returning, so all results are ordered on
+ *     `stream` exactly as if everything ran on it; stream capture of
+ *     `stream` captures both.
  *   - Outputs are overwritten, never accumulated into. Inputs must not
  *     overlap outputs or the workspace.
  *   - Workspace: `ws` is device scratch of at least the size returned by the

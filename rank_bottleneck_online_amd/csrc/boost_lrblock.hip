@@ -345,6 +345,56 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 inline size_t esize(int dtype) { return dtype == BOOST_DT_F32 ? 4 : 2; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// ---------------------------------------------------------------------------
+// Side stream. The weight-gradient products of a backward pass depend on the
+// input-gradient chain but nothing on that chain depends on them, so they run
+// on a second stream that forks from the caller's stream (event record +
+// wait) and joins it before the call returns: they fill the CUs that the
+// chain's kernels leave idle (partial last waves, the 172-tile dA2 product,
+// HBM-bound epilogues). One side stream and a few events per host thread and
+// device, created on first use with the default priority and never
+// destroyed; the library still allocates no device memory. Stream capture
+// follows the fork and the join, so a captured backward stays one graph.
+// ---------------------------------------------------------------------------
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[4] = {};
+  int next = 0;
+};
+
+int side_for_device(Side** out) {
+  constexpr int kMaxDev = 64;
+  thread_local Side sides[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BOOST_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDev) return fail(BOOST_ERR_UNSUPPORTED, "device index %d", dev);
+  Side& sd = sides[dev];
+  if (!sd.s) {
+    e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      sd.s = nullptr;
+      return fail(BOOST_ERR_LAUNCH, "hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+    }
+    for (hipEvent_t& ev : sd.ev) {
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return fail(BOOST_ERR_LAUNCH, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+    }
+  }
+  *out = &sd;
+  return BOOST_OK;
+}
+
+// `to` waits for everything enqueued on `from` so far.
+int stream_after(hipStream_t to, hipStream_t from, Side* sd) {
+  hipEvent_t ev = sd->ev[sd->next];
+  sd->next = (sd->next + 1) % 4;
+  hipError_t e = hipEventRecord(ev, from);
+  if (e == hipSuccess) e = hipStreamWaitEvent(to, ev, 0);
+  if (e != hipSuccess) return fail(BOOST_ERR_LAUNCH, "stream fork/join: %s", hipGetErrorString(e));
+  return BOOST_OK;
+}
+
 // ===========================================================================
 // Grouped block
 // ===========================================================================
@@ -449,7 +499,7 @@ int lrblock_bwd_core(int dt, int act, int norm, int64_t T, int64_t D, int64_t r,
                      const float* H, const float* sumsq, const void* dY, void* dx, float* dg, float* dA_cat,
                      float* dB, void* S, bool S_ready, void* dU, float* qpart, float* dgpart, float* partial,
                      const Choice& c_ds, const Choice& c_dB, const Choice& c_dA, const Choice& c_dx,
-                     hipStream_t s, const BwdLabels& L) {
+                     hipStream_t s, const BwdLabels& L, Side* side) {
   const int64_t es = esize(dt);
   const float inv = norm ? 1.f / (float)d_norm : 0.f;
   // dS_j = dY_j @ B_j^T, fused: dH, dU = rho dH, S = act(H), row partials q.
@@ -465,19 +515,23 @@ int lrblock_bwd_core(int dt, int act, int norm, int64_t T, int64_t D, int64_t r,
       RBO_TRY((gemm<EpiDS<false>, true, true, 1>(L.ds, dt, c_ds, T, r, n, G, ops, ea, s)));
     }
   }
+  // The weight gradients go to the side stream (it waits for dS, which
+  // produces dU and, here, S); dx stays on the caller's stream.
+  const hipStream_t sw = side ? side->s : s;
+  if (side) RBO_TRY(stream_after(sw, s, side));
   // dB_j = S_j^T @ dY_j  (K = T).
   {
     GemmOps ops{};
     ops.a[0] = opnd(S, G * r, T, r, es, r);
     ops.b[0] = opnd(dY, n, T, n, es, T * n);
-    RBO_TRY(wgrad(L.dB, dt, c_dB, r, n, T, G, ops, nullptr, dB, partial, s));
+    RBO_TRY(wgrad(L.dB, dt, c_dB, r, n, T, G, ops, nullptr, dB, partial, sw));
   }
   // dA_cat = diag(g) (x^T @ dU)  (K = T); the gain row scale is exact in fp32.
   {
     GemmOps ops{};
     ops.a[0] = opnd(x, D, T, D, es);
     ops.b[0] = opnd(dU, G * r, T, G * r, es);
-    RBO_TRY(wgrad(L.dA, dt, c_dA, D, G * r, T, 1, ops, norm ? g : nullptr, dA_cat, partial, s));
+    RBO_TRY(wgrad(L.dA, dt, c_dA, D, G * r, T, 1, ops, norm ? g : nullptr, dA_cat, partial, sw));
   }
   // dx~ = dU @ A_cat^T, fused with the RMSNorm backward and dg partials.
   {
@@ -493,6 +547,8 @@ int lrblock_bwd_core(int dt, int act, int norm, int64_t T, int64_t D, int64_t r,
       RBO_TRY((gemm<EpiStore<false>, true, true, 1>(L.dx, dt, c_dx, T, D, G * r, 1, ops, ea, s)));
     }
   }
+  // Join: the caller's stream waits for the weight gradients.
+  if (side) RBO_TRY(stream_after(s, sw, side));
   return BOOST_OK;
 }
 
@@ -702,12 +758,14 @@ int boost_lrblock_bwd(const boost_lrblock_desc* d, const void* x, const void* g,
   };
   RBO_TRY(check_ranges(rs));
   RBO_TRY(check_ws(ws, ws_bytes, p.bwd_bytes));
+  Side* side = nullptr;
+  RBO_TRY(side_for_device(&side));
   return lrblock_bwd_core(d->dtype, d->act, d->norm, d->T, d->d, d->r, d->G, d->d_out, d->eps, d->d_norm, x, g,
                           A_cat, B, H, sumsq, dY, dx, dg, dA_cat, dB, at(ws, p.b_S), false, at(ws, p.b_dU),
                           d->norm ? reinterpret_cast<float*>(at(ws, p.b_q)) : nullptr,
                           d->norm ? reinterpret_cast<float*>(at(ws, p.b_dg)) : nullptr,
                           p.b_part ? reinterpret_cast<float*>(at(ws, p.b_part)) : nullptr, p.ds, p.dB, p.dA, p.dx,
-                          as_stream(stream), kLrblockLabels);
+                          as_stream(stream), kLrblockLabels, side);
 }
 
 // ---------------------------------- MLP -----------------------------------
@@ -833,6 +891,8 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
   float* q = reinterpret_cast<float*>(at(ws, p.b_q));
   float* dgp = reinterpret_cast<float*>(at(ws, p.b_dg));
   float* part = p.b_part ? reinterpret_cast<float*>(at(ws, p.b_part)) : nullptr;
+  Side* side = nullptr;
+  RBO_TRY(side_for_device(&side));
   {  // dS2 = dY @ B2^T; dU2 = dS2 * act'(H2); S2 = act(H2)
     GemmOps ops{};
     ops.a[0] = opnd(dY, D, T, D, es);
@@ -840,11 +900,13 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
     EpiDS<false>::Args ea{H2, r, r, dU2, S2, nullptr, T, nullptr, 0.f, 0.f, d->act};
     RBO_TRY((gemm<EpiDS<false>, true, true, 1>("mlp_ds2", dt, p.ds2, T, r, D, 1, ops, ea, s)));
   }
+  // Weight gradients on the side stream, each after what it reads is ready.
+  RBO_TRY(stream_after(side->s, s, side));
   {  // dB2 = S2^T @ dY
     GemmOps ops{};
     ops.a[0] = opnd(S2, r, T, r, es);
     ops.b[0] = opnd(dY, D, T, D, es);
-    RBO_TRY(wgrad("mlp_dB2", dt, p.dB2, r, D, T, 1, ops, nullptr, dB2, part, s));
+    RBO_TRY(wgrad("mlp_dB2", dt, p.dB2, r, D, T, 1, ops, nullptr, dB2, part, side->s));
   }
   {  // dM = dU2 @ A2^T (fp32, kept unrounded for the SwiGLU backward)
     GemmOps ops{};
@@ -866,15 +928,18 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
     EpiSwigluBwd::Args ea{dM, Mr, dYgu, F, T * F};
     RBO_TRY((gemm<EpiSwigluBwd, true, true, 2>("mlp_recompute_swiglu_bwd", dt, p.rec, T, F, r, 1, ops, ea, s)));
   }
+  RBO_TRY(stream_after(side->s, s, side));
   {  // dA2 = M^T @ dU2
     GemmOps ops{};
     ops.a[0] = opnd(Mr, F, T, F, es);
     ops.b[0] = opnd(dU2, r, T, r, es);
-    RBO_TRY(wgrad("mlp_dA2", dt, p.dA2, F, r, T, 1, ops, nullptr, dA2, part, s));
+    RBO_TRY(wgrad("mlp_dA2", dt, p.dA2, F, r, T, 1, ops, nullptr, dA2, part, side->s));
   }
-  // Block 1 backward with dY = (dYg, dYu); S1 already recomputed.
+  // Block 1 backward with dY = (dYg, dYu); S1 already recomputed. It joins
+  // the side stream back into the caller's before returning.
   return lrblock_bwd_core(dt, d->act, 1, T, D, r, 2, F, d->eps, D, x, g, A1_cat, B1, H1, sumsq, dYgu, dx, dg,
-                          dA1_cat, dB1, S1, true, dU1, q, dgp, part, p.ds1, p.dB1, p.dA1, p.dx1, s, kMlp1Labels);
+                          dA1_cat, dB1, S1, true, dU1, q, dgp, part, p.ds1, p.dB1, p.dA1, p.dx1, s, kMlp1Labels,
+                          side);
 }
 
 // --------------------------- tensor-parallel share -------------------------
@@ -977,17 +1042,21 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
     RBO_TRY((gemm<EpiBtpUBwd, true, true, 1>("btp_u_bwd", dt, p.u, T, S, r, 1, ops, ea, st)));
   }
   RBO_TRY(launch_colsum(dgp, p.u.tiles_m, S, S, dg_s, st));
+  // Weight gradients on the side stream; dz on the caller's.
+  Side* side = nullptr;
+  RBO_TRY(side_for_device(&side));
+  RBO_TRY(stream_after(side->s, st, side));
   {  // dA_s = ag^T @ dp
     GemmOps ops{};
     ops.a[0] = opnd(ag, S, T, S, es);
     ops.b[0] = opnd(dp, r, T, r, es);
-    RBO_TRY(wgrad("btp_dA", dt, p.dA, S, r, T, 1, ops, nullptr, dA_s, part, st));
+    RBO_TRY(wgrad("btp_dA", dt, p.dA, S, r, T, 1, ops, nullptr, dA_s, part, side->s));
   }
   {  // dB_s = z^T @ du
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);
     ops.b[0] = opnd(du, S, T, S, es);
-    RBO_TRY(wgrad("btp_dB", dt, p.dB, r, S, T, 1, ops, nullptr, dB_s, part, st));
+    RBO_TRY(wgrad("btp_dB", dt, p.dB, r, S, T, 1, ops, nullptr, dB_s, part, side->s));
   }
   {  // dz = du @ B_s^T
     GemmOps ops{};
@@ -996,6 +1065,7 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
     EpiStore<false>::Args ea{dz, r, 0, nullptr};
     RBO_TRY((gemm<EpiStore<false>, true, true, 1>("btp_dz", dt, p.dz, T, r, S, 1, ops, ea, st)));
   }
+  RBO_TRY(stream_after(st, side->s, side));
   return BOOST_OK;
 }
 
