@@ -592,7 +592,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
         } else {
           __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
         }
-        if constexpr (RSS) static_for<0, C::FM>([&](auto i) { ss[i] = frag_sumsq(fa[cur][i], ss[i]); });
+        // The WN waves of a wave row hold the same A fragments; each takes
+        // every WN-th sub-step (a wave-uniform branch), so the sums cost each
+        // wave 1/WN of the dot products.
+        if constexpr (RSS) {
+          if (wn == kk % C::WN) static_for<0, C::FM>([&](auto i) { ss[i] = frag_sumsq(fa[cur][i], ss[i]); });
+        }
       });
     };
 
@@ -646,13 +651,22 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
 
   float* rowv = reinterpret_cast<float*>(smem + C::SCR_BYTES);
   float* colv = rowv + C::BM;
+  float* rowpart = colv + C::BN;  // [WN][BM]
   if constexpr (RSS) {
-    // Lanes l and l+32 hold the two k halves of the same row; waves in the
-    // same wave row saw the same A rows, so wave column 0 publishes.
+    // Lanes l and l+32 hold the two k halves of the same row; each wave of a
+    // wave row holds the sums over its share of the sub-steps. They are
+    // added in wave-column order, so the result is reproducible.
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
       const float s = ss[i] + __shfl_xor(ss[i], 32);
-      if (wn == 0 && lane < 32) rowv[wm * C::WTM + i * 32 + lane] = s;
+      if (lane < 32) rowpart[wn * C::BM + wm * C::WTM + i * 32 + lane] = s;
+    }
+    __syncthreads();
+    for (int r = t; r < C::BM; r += C::NT) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::WN; ++w) s += rowpart[w * C::BM + r];
+      rowv[r] = s;
     }
     __syncthreads();
   }
@@ -661,7 +675,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
   c.m0 = m0; c.n0 = n0; c.tm = tm; c.tn = tn; c.bidx = bidx; c.split = split; c.prob = prob;
   c.M = g.M; c.N = g.N; c.t = t; c.lane = lane; c.wave = wave; c.wm = wm; c.wn = wn;
   c.smem = smem; c.rowv = rowv; c.colv = colv;
-  c.rowpart = colv + C::BN;
+  c.rowpart = rowpart;
   c.colpart = c.rowpart + C::WN * C::BM;
   epilogue<C, E>(acc, c, ea);
 }
