@@ -70,6 +70,11 @@ template <> struct Vec8<bf16> {
 // Defaults for functors that need no preparation or reductions.
 struct EpiBase {
   static constexpr bool kRowSumsq = false, kRowSum = false, kColSum = false;
+  // Global inputs of one apply() call, loaded by pre() ahead of time (the
+  // driver issues every pre() of a 32-row chunk before staging it).
+  struct Pre {};
+  template <class C, class A>
+  static __device__ __forceinline__ void pre(const TileCtx&, const A&, int, int, Pre&) {}
   template <class C, class A>
   static __device__ __forceinline__ void begin(const TileCtx&, const A&) {}
   template <class C, class A>
@@ -99,7 +104,7 @@ struct EpiStore : EpiBase {
   }
   template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&)[8]) {
     typedef typename C::T T;
     typedef typename std::conditional<F32, float, T>::type O;
     const int row = c.m0 + lr, col = c.n0 + lc;
@@ -141,7 +146,7 @@ struct EpiDown : EpiBase {
   }
   template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&)[8]) {
     typedef typename C::T T;
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
@@ -168,7 +173,7 @@ struct EpiSwiglu : EpiBase {
   };
   template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&)[8]) {
     typedef typename C::T T;
     static_assert(C::NACC == 2, "SwiGLU needs two accumulators");
     const int row = c.m0 + lr, col = c.n0 + lc;
@@ -189,6 +194,9 @@ struct EpiSwiglu : EpiBase {
 template <bool NORM>
 struct EpiDS : EpiBase {
   static constexpr bool kRowSum = NORM;
+  struct Pre {
+    float h[8];
+  };
   struct Args {
     const float* H;
     int64_t ld;        // columns of H, dU, S (= G*r)
@@ -208,15 +216,21 @@ struct EpiDS : EpiBase {
         c.rowv[r] = c.m0 + r < c.M ? rms_scale(a.sumsq[c.m0 + r], a.inv_dnorm, a.eps) : 0.f;
   }
   template <class C>
+  static __device__ __forceinline__ void pre(const TileCtx& c, const Args& a, int lr, int lc, Pre& pf) {
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    Vec8<float>::load(a.H, (int64_t)row * a.ld + (int64_t)c.bidx * a.r + col, pf.h);
+  }
+  template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float& rowc, float (&)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float& rowc, float (&)[8]) {
     typedef typename C::T T;
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
     const int64_t o = (int64_t)row * a.ld + (int64_t)c.bidx * a.r + col;
     const float rho = NORM ? c.rowv[lr] : 1.f;
-    float h[8], du[8], sv[8];
-    Vec8<float>::load(a.H, o, h);
+    float du[8], sv[8];
+    const float (&h)[8] = pf.h;
     float q = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -246,6 +260,9 @@ struct EpiDS : EpiBase {
 // ---------------------------------------------------------------------------
 struct EpiDX : EpiBase {
   static constexpr bool kColSum = true;
+  struct Pre {
+    float x[8], g[8];
+  };
   struct Args {
     const void* x;
     const void* g;
@@ -273,16 +290,24 @@ struct EpiDX : EpiBase {
     }
   }
   template <class C>
+  static __device__ __forceinline__ void pre(const TileCtx& c, const Args& a, int lr, int lc, Pre& pf) {
+    typedef typename C::T T;
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    Vec8<T>::load(a.x, (int64_t)row * a.ld + col, pf.x);
+    Vec8<T>::load(a.g, col, pf.g);
+  }
+  template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float&, float (&colc)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&colc)[8]) {
     typedef typename C::T T;
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
     const int64_t o = (int64_t)row * a.ld + col;
     const float coef = c.rowv[lr];
-    float xv[8], gv[8], dx[8];
-    Vec8<T>::load(a.x, o, xv);
-    Vec8<T>::load(a.g, col, gv);
+    float dx[8];
+    const float (&xv)[8] = pf.x;
+    const float (&gv)[8] = pf.g;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       dx[e] = gv[e] * v[0][e] - coef * xv[e];
@@ -303,6 +328,9 @@ struct EpiDX : EpiBase {
 // dYg = dM Yu SiLU'(Yg), dYu = dM SiLU(Yg) into a [2,T,ffn] buffer.
 // ---------------------------------------------------------------------------
 struct EpiSwigluBwd : EpiBase {
+  struct Pre {
+    float dm[8];
+  };
   struct Args {
     const float* dM;
     void* M;
@@ -311,15 +339,21 @@ struct EpiSwigluBwd : EpiBase {
     int64_t ystride; // T * ffn
   };
   template <class C>
+  static __device__ __forceinline__ void pre(const TileCtx& c, const Args& a, int lr, int lc, Pre& pf) {
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    Vec8<float>::load(a.dM, (int64_t)row * a.ld + col, pf.dm);
+  }
+  template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&)[8]) {
     typedef typename C::T T;
     static_assert(C::NACC == 2, "SwiGLU backward needs two accumulators");
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
     const int64_t o = (int64_t)row * a.ld + col;
-    float dm[8], m[8], dg[8], du[8];
-    Vec8<float>::load(a.dM, o, dm);
+    float m[8], dg[8], du[8];
+    const float (&dm)[8] = pf.dm;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float yg = v[0][e], yu = v[1][e];
@@ -351,7 +385,7 @@ struct EpiBtpU : EpiBase {
   };
   template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float& rowc, float (&)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float& rowc, float (&)[8]) {
     typedef typename C::T T;
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
@@ -401,7 +435,7 @@ struct EpiBtpP : EpiBase {
   }
   template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float&, float (&)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&)[8]) {
     typedef typename C::T T;
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
@@ -421,6 +455,9 @@ struct EpiBtpP : EpiBase {
 // ---------------------------------------------------------------------------
 struct EpiBtpUBwd : EpiBase {
   static constexpr bool kColSum = true;
+  struct Pre {
+    float e[8], g[8];
+  };
   struct Args {
     const float* e;
     const float* ds;
@@ -435,16 +472,24 @@ struct EpiBtpUBwd : EpiBase {
     for (int r = c.t; r < C::BM; r += C::NT) c.rowv[r] = c.m0 + r < c.M ? a.ds[c.m0 + r] : 0.f;
   }
   template <class C>
+  static __device__ __forceinline__ void pre(const TileCtx& c, const Args& a, int lr, int lc, Pre& pf) {
+    typedef typename C::T T;
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    Vec8<float>::load(a.e, (int64_t)row * a.ld + col, pf.e);
+    Vec8<T>::load(a.g, col, pf.g);
+  }
+  template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], float&, float (&colc)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&colc)[8]) {
     typedef typename C::T T;
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
     const int64_t o = (int64_t)row * a.ld + col;
     const float dsv = c.rowv[lr];
-    float ev[8], gv[8], du[8], ag[8];
-    Vec8<float>::load(a.e, o, ev);
-    Vec8<T>::load(a.g, col, gv);
+    float du[8], ag[8];
+    const float (&ev)[8] = pf.e;
+    const float (&gv)[8] = pf.g;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float u = v[0][e];

@@ -395,7 +395,8 @@ __device__ __forceinline__ void group_tile(int tile, int tiles_m, int tiles_n, i
 //   kRowSumsq           the A loader accumulates row sums of squares into rowv
 //   kRowSum / kColSum   the reductions above are wanted
 //   begin(c, a)         per-tile preparation (all threads; a barrier follows)
-//   apply(c, a, lr, lc, v, rowc, colc)   lr/lc tile-local row / first column
+//   Pre, pre(c, a, lr, lc, pf)   global inputs of one apply, loaded early
+//   apply(c, a, lr, lc, v, pf, rowc, colc)   lr/lc tile-local row / first column
 //   rows_done(c, a, sums) / cols_done(c, a, sums)   sums in LDS, BM / BN long
 // ---------------------------------------------------------------------------
 template <class C, class E>
@@ -417,6 +418,12 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
   for (int e = 0; e < 8; ++e) colc[e] = 0.f;
 
   static_for<0, C::FM>([&](auto i) {
+    // The chunk's global inputs are requested first, so their latency
+    // overlaps the staging, the barrier and each other.
+    typename E::Pre pf[STEPS];
+    static_for<0, STEPS>([&](auto s) {
+      E::template pre<C>(c, ea, c.wm * C::WTM + i * 32 + s * RPS + rsub, c.wn * C::WTN + c8 * 8, pf[s]);
+    });
     static_for<0, C::NACC>([&](auto p) {
       static_for<0, C::FN>([&](auto j) {
         static_for<0, 16>([&](auto v) {
@@ -426,7 +433,7 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
       });
     });
     __syncthreads();
-    for (int s = 0; s < STEPS; ++s) {
+    static_for<0, STEPS>([&](auto s) {
       const int r = s * RPS + rsub;
       const int lr = c.wm * C::WTM + i * 32 + r;
       const int lc = c.wn * C::WTN + c8 * 8;
@@ -439,13 +446,13 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
         vals[p][4] = b.x; vals[p][5] = b.y; vals[p][6] = b.z; vals[p][7] = b.w;
       });
       float rowc = 0.f;
-      E::template apply<C>(c, ea, lr, lc, vals, rowc, colc);
+      E::template apply<C>(c, ea, lr, lc, vals, pf[s], rowc, colc);
       if constexpr (E::kRowSum) {
 #pragma unroll
         for (int m = 1; m < V8; m <<= 1) rowc += __shfl_xor(rowc, m);
         if (c8 == 0) c.rowpart[c.wn * C::BM + lr] = rowc;
       }
-    }
+    });
     __syncthreads();
   });
 
