@@ -64,8 +64,7 @@ def mlp_kernel_flops(T, d, r, ffn):
         "mlp_up2": 2 * T * r * d,
         "mlp_ds2": 2 * T * d * r,
         "mlp_dB2": 2 * r * d * T,
-        "mlp_dM": 2 * T * r * ffn,
-        "mlp_recompute_swiglu_bwd": 2 * 2 * T * r * ffn,
+        "mlp_recompute_swiglu_bwd": 3 * 2 * T * r * ffn,  # gate and up recompute + dM, one launch
         "mlp_dA2": 2 * ffn * r * T,
         "mlp1_ds": 2 * 2 * T * ffn * r,
         "mlp1_dB": 2 * 2 * r * ffn * T,
@@ -82,7 +81,15 @@ def lrblock_kernel_flops(T, d, r, G, n, bwd=True):
     return f
 
 
-RECOMPUTE_LABELS = ("mlp_recompute_swiglu_bwd", "btp_u_bwd")
+def recompute_flops(kind, w) -> float:
+    """Flops of the prescribed recompute in one step (the gate/up re-forward
+    of each MLP, u of the BTP share)."""
+    mlp = 2 * 2 * w["T"] * w["r"] * w.get("ffn", 0)
+    if kind in ("lrmlp", "layerset"):
+        return float(mlp)
+    if kind == "btp":
+        return float(2 * w["T"] * w["r"] * (w["d_global"] // w["P"]))
+    return 0.0
 # Launches the library puts on its side stream (weight gradients): they run
 # concurrently with the input-gradient chain, so their event durations
 # include sharing the GPU and they are not roofline candidates.
@@ -248,19 +255,20 @@ class Workload:
         """Algorithmic flops of one step; model_only drops the prescribed
         recompute (the gate/up re-forward of the MLP, u of the BTP share)."""
         w = self.w
+        sub = recompute_flops(self.kind, w) if model_only else 0.0
 
         def tot(f):
-            return float(sum(v for k, v in f.items() if not (model_only and k in RECOMPUTE_LABELS)))
+            return float(sum(f.values()))
 
         if self.kind == "lrmlp":
-            return tot(mlp_kernel_flops(w["T"], w["d"], w["r"], w["ffn"]))
+            return tot(mlp_kernel_flops(w["T"], w["d"], w["r"], w["ffn"])) - sub
         if self.kind == "lrblock":
-            return tot(lrblock_kernel_flops(w["T"], w["d"], w["r"], w["G"], w["d_out"], self.bwd))
+            return tot(lrblock_kernel_flops(w["T"], w["d"], w["r"], w["G"], w["d_out"], self.bwd)) - sub
         if self.kind == "btp":
-            return tot(btp_kernel_flops(w["T"], w["r"], w["d_global"] // w["P"]))
+            return tot(btp_kernel_flops(w["T"], w["r"], w["d_global"] // w["P"])) - sub
         T, d, r, ffn = w["T"], w["d"], w["r"], w["ffn"]
         return (tot(lrblock_kernel_flops(T, d, r, 3, d)) + tot(lrblock_kernel_flops(T, d, r, 1, d)) +
-                tot(mlp_kernel_flops(T, d, r, ffn)))
+                tot(mlp_kernel_flops(T, d, r, ffn))) - sub
 
 
 # ---------------------------------------------------------------------------

@@ -160,7 +160,7 @@ int gemm(const char* label, int dtype, const Choice& ch, int64_t M, int64_t N, i
          const GemmOps& ops, const typename E::Args& ea, hipStream_t s) {
   const int m = (int)M, n = (int)N, k = (int)K, b = (int)batch;
   if (dtype == BOOST_DT_F32) return launch_cfg<CF32<AKC, BKC, NACC>, E>(label, ch, m, n, k, b, ops, ea, s);
-  if constexpr (NACC == 2) {
+  if constexpr (NACC >= 2) {
     return launch_cfg<C256x128<AKC, BKC, NACC>, E>(label, ch, m, n, k, b, ops, ea, s);
   } else {
     switch (ch.id) {
@@ -572,9 +572,9 @@ int lrmlp_check_desc(const boost_lrmlp_desc* d) {
 
 struct LrmlpPlan {
   Choice down1, dual, down2, up2;                       // forward
-  Choice ds2, dB2, dM, rec, dA2, ds1, dB1, dA1, dx1;    // backward
+  Choice ds2, dB2, rec, dA2, ds1, dB1, dA1, dx1;        // backward
   size_t f_A1T, f_B1T, f_A2T, f_B2T, f_S1, f_M, f_S2, fwd_bytes;
-  size_t b_B1T, b_S2, b_dU2, b_dM, b_S1, b_M, b_dY, b_dU1, b_q, b_dg, b_part, bwd_bytes;
+  size_t b_B1T, b_S2, b_dU2, b_S1, b_M, b_dY, b_dU1, b_q, b_dg, b_part, bwd_bytes;
 };
 
 LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
@@ -587,7 +587,6 @@ LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
   p.up2 = choose(dt, T, D, r, 1, false, false);
   p.ds2 = choose(dt, T, r, D, 1, false, false);
   p.dB2 = choose(dt, r, D, T, 1, true, false);
-  p.dM = choose(dt, T, F, r, 1, false, false);
   p.rec = p.dual;
   p.dA2 = choose(dt, F, r, T, 1, true, false);
   p.ds1 = choose(dt, T, r, F, 2, false, false);
@@ -607,7 +606,6 @@ LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
   p.b_B1T = b.take((size_t)(2 * r * F * es));
   p.b_S2 = b.take((size_t)(T * r * es));
   p.b_dU2 = b.take((size_t)(T * r * es));
-  p.b_dM = b.take((size_t)(T * F * 4));
   p.b_S1 = b.take((size_t)(T * 2 * r * es));
   p.b_M = b.take((size_t)(T * F * es));
   p.b_dY = b.take((size_t)(2 * T * F * es));
@@ -883,7 +881,6 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
   hipStream_t s = as_stream(stream);
   void* S2 = at(ws, p.b_S2);
   void* dU2 = at(ws, p.b_dU2);
-  float* dM = reinterpret_cast<float*>(at(ws, p.b_dM));
   void* S1 = at(ws, p.b_S1);
   void* Mr = at(ws, p.b_M);
   void* dYgu = at(ws, p.b_dY);
@@ -908,25 +905,20 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
     ops.b[0] = opnd(dY, D, T, D, es);
     RBO_TRY(wgrad("mlp_dB2", dt, p.dB2, r, D, T, 1, ops, nullptr, dB2, part, side->s));
   }
-  {  // dM = dU2 @ A2^T (fp32, kept unrounded for the SwiGLU backward)
-    GemmOps ops{};
-    ops.a[0] = opnd(dU2, r, T, r, es);
-    ops.b[0] = opnd(A2, r, F, r, es);
-    EpiStore<true>::Args ea{dM, F, 0, nullptr};
-    RBO_TRY((gemm<EpiStore<true>, true, true, 1>("mlp_dM", dt, p.dM, T, F, r, 1, ops, ea, s)));
-  }
   // S1 = act(H1) recomputed from the saved bottleneck.
   RBO_TRY(launch_act_quant(dt, H1, S1, T * 2 * r, d->act, s));
   void* B1T = at(ws, p.b_B1T);
   RBO_TRY(launch_transpose(dt, B1, nullptr, B1T, r, F, 2, s));
-  {  // recompute Yg, Yu; M, dYg, dYu
+  {  // recompute Yg, Yu and dM = dU2 @ A2^T in the same tile; M, dYg, dYu
     GemmOps ops{};
     ops.a[0] = opnd(S1, 2 * r, T, r, es);
     ops.a[1] = opnd(static_cast<const char*>(S1) + r * es, 2 * r, T, r, es);
+    ops.a[2] = opnd(dU2, r, T, r, es);
     ops.b[0] = opnd(B1T, r, F, r, es);
     ops.b[1] = opnd(static_cast<const char*>(B1T) + F * r * es, r, F, r, es);
-    EpiSwigluBwd::Args ea{dM, Mr, dYgu, F, T * F};
-    RBO_TRY((gemm<EpiSwigluBwd, true, true, 2>("mlp_recompute_swiglu_bwd", dt, p.rec, T, F, r, 1, ops, ea, s)));
+    ops.b[2] = opnd(A2, r, F, r, es);
+    EpiSwigluBwd::Args ea{Mr, dYgu, F, T * F};
+    RBO_TRY((gemm<EpiSwigluBwd, true, true, 3>("mlp_recompute_swiglu_bwd", dt, p.rec, T, F, r, 1, ops, ea, s)));
   }
   RBO_TRY(stream_after(side->s, s, side));
   {  // dA2 = M^T @ dU2

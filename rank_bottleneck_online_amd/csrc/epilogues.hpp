@@ -323,45 +323,36 @@ struct EpiDX : EpiBase {
 };
 
 // ---------------------------------------------------------------------------
-// SwiGLU backward with the gate/up recompute (two accumulators: Yg, Yu).
-// Reads dM (fp32); writes M = SiLU(Yg) Yu (operand of dA2), and
-// dYg = dM Yu SiLU'(Yg), dYu = dM SiLU(Yg) into a [2,T,ffn] buffer.
+// SwiGLU backward with the gate/up recompute, three accumulators over the
+// same [T-tile, ffn-tile]: Yg = S1_0 B1_0, Yu = S1_1 B1_1 and dM = dU2 A2^T
+// (all K = r). Writes M = SiLU(Yg) Yu (operand of dA2), and
+// dYg = dM Yu SiLU'(Yg), dYu = dM SiLU(Yg) into a [2,T,ffn] buffer; dM never
+// leaves the registers, unrounded.
 // ---------------------------------------------------------------------------
 struct EpiSwigluBwd : EpiBase {
-  struct Pre {
-    float dm[8];
-  };
   struct Args {
-    const float* dM;
     void* M;
     void* dYgu;
     int64_t ld;      // ffn
     int64_t ystride; // T * ffn
   };
   template <class C>
-  static __device__ __forceinline__ void pre(const TileCtx& c, const Args& a, int lr, int lc, Pre& pf) {
-    const int row = c.m0 + lr, col = c.n0 + lc;
-    if (row >= c.M || col >= c.N) return;
-    Vec8<float>::load(a.dM, (int64_t)row * a.ld + col, pf.dm);
-  }
-  template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&)[8]) {
+                                               const float (&v)[C::NACC][8], const Pre&, float&, float (&)[8]) {
     typedef typename C::T T;
-    static_assert(C::NACC == 2, "SwiGLU backward needs two accumulators");
+    static_assert(C::NACC == 3, "SwiGLU backward takes gate, up and dM accumulators");
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
     const int64_t o = (int64_t)row * a.ld + col;
     float m[8], dg[8], du[8];
-    const float (&dm)[8] = pf.dm;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float yg = v[0][e], yu = v[1][e];
+      const float yg = v[0][e], yu = v[1][e], dm = v[2][e];
       const float s = sigmoid_f(yg);
       const float sl = yg * s;
       m[e] = sl * yu;
-      dg[e] = dm[e] * yu * (s * (1.f + yg * (1.f - s)));
-      du[e] = dm[e] * sl;
+      dg[e] = dm * yu * (s * (1.f + yg * (1.f - s)));
+      du[e] = dm * sl;
     }
     Vec8<T>::store(a.M, o, m);
     Vec8<T>::store(a.dYgu, o, dg);

@@ -182,7 +182,10 @@ struct Cfg {
   // floats (the two half-waves of the MFMA layout then hit disjoint banks),
   // reusing the pipeline LDS.
   static constexpr int EPI_STR = WTN + 8;
-  static constexpr int EPI_SUB = 32 * EPI_STR;
+  // Accumulator rows staged per round: 32 (one MFMA block row), or 16 with
+  // three accumulators so the staging still fits next to the pipeline.
+  static constexpr int EPI_ROWS = NACC > 2 ? 16 : 32;
+  static constexpr int EPI_SUB = EPI_ROWS * EPI_STR;
   static constexpr int EPI_BYTES = WM * WN * NACC * EPI_SUB * 4;
   static constexpr int SCR_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
   // After that: per-row / per-column fp32 vectors and reduction partials.
@@ -212,7 +215,7 @@ struct GemmGeom {
 };
 
 struct GemmOps {
-  Operand a[2], b[2];  // one pair per accumulator (NACC <= 2)
+  Operand a[3], b[3];  // one pair per accumulator (NACC <= 3)
 };
 
 // Per-tile context handed to the epilogue.
@@ -380,8 +383,8 @@ __device__ __forceinline__ void group_tile(int tile, int tiles_m, int tiles_n, i
 // ---------------------------------------------------------------------------
 // Epilogue driver.
 //
-// The accumulators are handed to the epilogue through LDS, 32 rows of each
-// wave's tile at a time: the wave writes them in the MFMA layout into its
+// The accumulators are handed to the epilogue through LDS, 32 rows (16 with
+// three accumulators) of each wave's tile at a time: the wave writes them in the MFMA layout into its
 // private padded buffer, then reads them back row-contiguously, 8 columns
 // per lane (a row of the wave tile is WTN/8 consecutive lanes). The
 // epilogue functor E sees (tile row, tile column, 8 values per accumulator)
@@ -403,10 +406,11 @@ template <class C, class E>
 __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN], const TileCtx& c,
                                          const typename E::Args& ea) {
   constexpr int STR = C::EPI_STR, SUB = C::EPI_SUB;
+  constexpr int ER = C::EPI_ROWS, ROUNDS = 32 / ER;
   constexpr int V8 = C::WTN / 8;        // lanes per row in the read-back
   constexpr int RPS = 64 / V8;          // rows per read-back step
-  constexpr int STEPS = 32 / RPS;
-  static_assert(64 % V8 == 0 && 32 % RPS == 0, "wave tile width must be 32, 64 or 128");
+  constexpr int STEPS = ER / RPS;       // read-back steps per staging round
+  static_assert(64 % V8 == 0 && ER % RPS == 0, "wave tile width must be 32, 64 or 128");
   float* scr = reinterpret_cast<float*>(c.smem) + c.wave * (C::NACC * SUB);
   const int c8 = c.lane % V8, rsub = c.lane / V8;
 
@@ -418,42 +422,47 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
   for (int e = 0; e < 8; ++e) colc[e] = 0.f;
 
   static_for<0, C::FM>([&](auto i) {
-    // The chunk's global inputs are requested first, so their latency
-    // overlaps the staging, the barrier and each other.
-    typename E::Pre pf[STEPS];
-    static_for<0, STEPS>([&](auto s) {
-      E::template pre<C>(c, ea, c.wm * C::WTM + i * 32 + s * RPS + rsub, c.wn * C::WTN + c8 * 8, pf[s]);
-    });
-    static_for<0, C::NACC>([&](auto p) {
-      static_for<0, C::FN>([&](auto j) {
-        static_for<0, 16>([&](auto v) {
-          constexpr int r0 = (v >> 2) * 8 + (v & 3);
-          scr[p * SUB + (r0 + (c.lane >> 5) * 4) * STR + j * 32 + (c.lane & 31)] = acc[p][i][j][v()];
+    static_for<0, ROUNDS>([&](auto h) {
+      // The chunk's global inputs are requested first, so their latency
+      // overlaps the staging, the barrier and each other.
+      typename E::Pre pf[STEPS];
+      static_for<0, STEPS>([&](auto s) {
+        E::template pre<C>(c, ea, c.wm * C::WTM + i * 32 + h * ER + s * RPS + rsub, c.wn * C::WTN + c8 * 8,
+                           pf[s]);
+      });
+      // MFMA register v holds row 8 (v/4) + 4 (lane/32) + v%4 of the block;
+      // registers [16h/ROUNDS, 16(h+1)/ROUNDS) cover rows [h ER, (h+1) ER).
+      static_for<0, C::NACC>([&](auto p) {
+        static_for<0, C::FN>([&](auto j) {
+          static_for<h * (16 / ROUNDS), (h + 1) * (16 / ROUNDS)>([&](auto v) {
+            constexpr int r0 = (v >> 2) * 8 + (v & 3) - h * ER;
+            scr[p * SUB + (r0 + (c.lane >> 5) * 4) * STR + j * 32 + (c.lane & 31)] = acc[p][i][j][v()];
+          });
         });
       });
-    });
-    __syncthreads();
-    static_for<0, STEPS>([&](auto s) {
-      const int r = s * RPS + rsub;
-      const int lr = c.wm * C::WTM + i * 32 + r;
-      const int lc = c.wn * C::WTN + c8 * 8;
-      float vals[C::NACC][8];
-      static_for<0, C::NACC>([&](auto p) {
-        const float* src = scr + p * SUB + r * STR + c8 * 8;
-        const float4 a = *reinterpret_cast<const float4*>(src);
-        const float4 b = *reinterpret_cast<const float4*>(src + 4);
-        vals[p][0] = a.x; vals[p][1] = a.y; vals[p][2] = a.z; vals[p][3] = a.w;
-        vals[p][4] = b.x; vals[p][5] = b.y; vals[p][6] = b.z; vals[p][7] = b.w;
-      });
-      float rowc = 0.f;
-      E::template apply<C>(c, ea, lr, lc, vals, pf[s], rowc, colc);
-      if constexpr (E::kRowSum) {
+      __syncthreads();
+      static_for<0, STEPS>([&](auto s) {
+        const int r = s * RPS + rsub;
+        const int lr = c.wm * C::WTM + i * 32 + h * ER + r;
+        const int lc = c.wn * C::WTN + c8 * 8;
+        float vals[C::NACC][8];
+        static_for<0, C::NACC>([&](auto p) {
+          const float* src = scr + p * SUB + r * STR + c8 * 8;
+          const float4 a = *reinterpret_cast<const float4*>(src);
+          const float4 b = *reinterpret_cast<const float4*>(src + 4);
+          vals[p][0] = a.x; vals[p][1] = a.y; vals[p][2] = a.z; vals[p][3] = a.w;
+          vals[p][4] = b.x; vals[p][5] = b.y; vals[p][6] = b.z; vals[p][7] = b.w;
+        });
+        float rowc = 0.f;
+        E::template apply<C>(c, ea, lr, lc, vals, pf[s], rowc, colc);
+        if constexpr (E::kRowSum) {
 #pragma unroll
-        for (int m = 1; m < V8; m <<= 1) rowc += __shfl_xor(rowc, m);
-        if (c8 == 0) c.rowpart[c.wn * C::BM + lr] = rowc;
-      }
+          for (int m = 1; m < V8; m <<= 1) rowc += __shfl_xor(rowc, m);
+          if (c8 == 0) c.rowpart[c.wn * C::BM + lr] = rowc;
+        }
+      });
+      __syncthreads();
     });
-    __syncthreads();
   });
 
   if constexpr (E::kColSum) {
