@@ -22,3 +22,10 @@ from .lrblock import (  # noqa: F401
     silu,
     silu_grad,
 )
+from .layer import (  # noqa: F401
+    layer_backward,
+    layer_forward,
+    round_to_bf16,
+    standin_backward,
+    standin_forward,
+)

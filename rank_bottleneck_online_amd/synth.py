@@ -178,6 +178,21 @@ def layerset_inputs(T, d, r, ffn, dtype="bf16", seed=0):
     }
 
 
+def layer_inputs(T, d, r, ffn, dtype="bf16", seed=0):
+    """Inputs of one chained decoder layer: the layer-set draws (same order),
+    of which the layer uses the QKV block's x as its input x, the MLP's dY as
+    the output gradient dh3, and every block's weights and gains."""
+    s = layerset_inputs(T, d, r, ffn, dtype, seed)
+    q, o, m = s["qkv"], s["o"], s["mlp"]
+    return {
+        "x": q["x"],
+        "qkv": {"g": q["g"], "A_cat": q["A_cat"], "B": q["B"]},
+        "o": {"A_cat": o["A_cat"], "B": o["B"]},
+        "mlp": {k: m[k] for k in ("g", "A1_cat", "B1", "A2", "B2")},
+        "dh3": m["dY"],
+    }
+
+
 # Named workloads (LLaMA-2-family shapes). T = batch * sequence length.
 WORKLOADS = {
     "tiny_qkv_f32": dict(kind="lrblock", T=64, d=256, r=64, G=3, d_out=256, dtype="f32"),
@@ -185,4 +200,5 @@ WORKLOADS = {
     "llama2_7b_mlp": dict(kind="lrmlp", T=8192, d=4096, r=1024, ffn=11008, dtype="bf16"),
     "llama2_13b_btp_share_tp4": dict(kind="btp", T=8192, r=1280, d_global=5120, P=4, dtype="bf16"),
     "llama2_40b_layerset": dict(kind="layerset", T=4096, d=8192, r=2048, ffn=22016, dtype="bf16"),
+    "llama2_40b_layer_chained": dict(kind="layer", T=4096, d=8192, r=2048, ffn=22016, dtype="bf16"),
 }
