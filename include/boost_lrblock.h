@@ -169,6 +169,55 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* desc, const void* x, const void* g,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Chaining blocks into a decoder layer (Online-RMSNorm, section 2.2: the
+ * statistic of a block's input is produced where that input is produced).
+ * The *_chained entry points extend the calls above; passing NULL for every
+ * extra argument gives exactly the plain call.
+ *   residual[T,d_out] (dtype, G = 1 only): the up product writes
+ *       Y = residual + S @ B (one rounding), e.g. h2 = x + O(a).
+ *   sumsq_next[T] (fp32 out, G = 1 only): the row sums of squares of the
+ *       stored Y (the dtype values, squared and summed in fp32) - the next
+ *       block's Online-RMSNorm statistic, formed from per-tile-column
+ *       partials in a fixed order.
+ *   sumsq_in[T] (fp32, norm = 1 only): the statistic of x from its producer;
+ *       the down product then takes its 1/rms row scale from it instead of
+ *       summing the squares of x itself. `sumsq` may then be NULL; when not
+ *       NULL it receives a copy.
+ *   dx_add[T,d] (dtype, backward, norm = 1 only): added to dx in the
+ *       input-gradient epilogue (the residual path of the layer's gradient).
+ * The forward workspace sizes above already cover the chained forms.
+ * ------------------------------------------------------------------------ */
+int boost_lrblock_fwd_chained(const boost_lrblock_desc* desc, const void* x, const void* g,
+                              const void* A_cat, const void* B, const void* residual,
+                              const float* sumsq_in, void* Y, float* H, float* sumsq,
+                              float* sumsq_next, void* ws, size_t ws_bytes, void* stream);
+
+int boost_lrblock_bwd_chained(const boost_lrblock_desc* desc, const void* x, const void* g,
+                              const void* A_cat, const void* B, const float* H,
+                              const float* sumsq, const void* dY, const void* dx_add, void* dx,
+                              float* dg, float* dA_cat, float* dB, void* ws, size_t ws_bytes,
+                              void* stream);
+
+int boost_lrmlp_fwd_chained(const boost_lrmlp_desc* desc, const void* x, const void* g,
+                            const void* A1_cat, const void* B1, const void* A2, const void* B2,
+                            const void* residual, const float* sumsq_in, void* Y, float* H1,
+                            float* H2, float* sumsq, float* sumsq_next, void* ws,
+                            size_t ws_bytes, void* stream);
+
+int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* desc, const void* x, const void* g,
+                            const void* A1_cat, const void* B1, const void* A2, const void* B2,
+                            const float* H1, const float* H2, const float* sumsq, const void* dY,
+                            const void* dx_add, void* dx, float* dg, float* dA1_cat, float* dB1,
+                            float* dA2, float* dB2, void* ws, size_t ws_bytes, void* stream);
+
+/* Attention stand-in between a layer's QKV and O blocks (the attention core
+ * is not part of the bottleneck block): a[T,d] = q + k + v for qkv[3,T,d]
+ * (dtype; summed in fp32, one rounding), and its backward
+ * dqkv[3,T,d] = (da, da, da). d must be a multiple of 64. */
+int boost_attn_standin_fwd(int dtype, int64_t T, int64_t d, const void* qkv, void* a, void* stream);
+int boost_attn_standin_bwd(int dtype, int64_t T, int64_t d, const void* da, void* dqkv, void* stream);
+
+/* ------------------------------------------------------------------------
  * One tensor-parallel share of a bottleneck pair (BTP, section 2.1):
  *   u = z @ B_s            (column slice of the up projection)  [T,d_shard]
  *   a = SiLU(u)            (op on the sharded activation)

@@ -60,6 +60,12 @@ _SIGS = {
     "boost_lrmlp_workspace_size": ([ctypes.POINTER(LrmlpDesc), ctypes.c_int, ctypes.POINTER(_SZ)], ctypes.c_int),
     "boost_lrmlp_fwd": ([ctypes.POINTER(LrmlpDesc)] + [_VP] * 10 + [_VP, _SZ, _VP], ctypes.c_int),
     "boost_lrmlp_bwd": ([ctypes.POINTER(LrmlpDesc)] + [_VP] * 16 + [_VP, _SZ, _VP], ctypes.c_int),
+    "boost_lrblock_fwd_chained": ([ctypes.POINTER(LrblockDesc)] + [_VP] * 10 + [_VP, _SZ, _VP], ctypes.c_int),
+    "boost_lrblock_bwd_chained": ([ctypes.POINTER(LrblockDesc)] + [_VP] * 12 + [_VP, _SZ, _VP], ctypes.c_int),
+    "boost_lrmlp_fwd_chained": ([ctypes.POINTER(LrmlpDesc)] + [_VP] * 13 + [_VP, _SZ, _VP], ctypes.c_int),
+    "boost_lrmlp_bwd_chained": ([ctypes.POINTER(LrmlpDesc)] + [_VP] * 17 + [_VP, _SZ, _VP], ctypes.c_int),
+    "boost_attn_standin_fwd": ([ctypes.c_int, ctypes.c_int64, ctypes.c_int64, _VP, _VP, _VP], ctypes.c_int),
+    "boost_attn_standin_bwd": ([ctypes.c_int, ctypes.c_int64, ctypes.c_int64, _VP, _VP, _VP], ctypes.c_int),
     "boost_btp_share_workspace_size": ([ctypes.POINTER(BtpShareDesc), ctypes.c_int, ctypes.POINTER(_SZ)],
                                        ctypes.c_int),
     "boost_btp_share_fwd": ([ctypes.POINTER(BtpShareDesc)] + [_VP] * 6 + [_VP, _SZ, _VP], ctypes.c_int),
@@ -201,6 +207,66 @@ def lrblock_bwd(x, g, A_cat, B, H, sumsq, dY, act="silu", norm=True, eps=1e-5, d
     return dx, dg, dA, dB
 
 
+def lrblock_fwd_chained(x, g, A_cat, B, residual=None, sumsq_in=None, sumsq_next=False, act="silu", norm=True,
+                        eps=1e-5, d_norm=None, out=None, ws=None, stream=None):
+    """Forward inside a layer: Y = residual + S @ B (G = 1) when residual is
+    given, the statistic of x taken from sumsq_in when given, and the next
+    block's statistic sumsq_next[T] when asked. Returns (Y, H, sumsq or
+    None, sumsq_next or None)."""
+    T, d = x.shape
+    G, r, d_out = B.shape
+    desc = lrblock_desc(T, d, r, G, d_out, _dtype_code(x), act, norm, eps, d_norm)
+    if out is None:
+        out = (torch.empty((G, T, d_out), dtype=x.dtype, device=x.device), _f32((T, G * r), x.device),
+               _f32((T,), x.device) if norm and sumsq_in is None else None,
+               _f32((T,), x.device) if sumsq_next else None)
+    Y, H, sumsq, snext = out
+    ws = _ws(lrblock_workspace_size(desc, False), x.device, ws)
+    _check(lib().boost_lrblock_fwd_chained(ctypes.byref(desc), _ptr(x), _ptr(g) if norm else None, _ptr(A_cat),
+                                           _ptr(B), _ptr(residual), _ptr(sumsq_in), _ptr(Y), _ptr(H), _ptr(sumsq),
+                                           _ptr(snext), _ptr(ws), ws.numel(), _stream(stream)),
+           "boost_lrblock_fwd_chained")
+    return Y, H, sumsq, snext
+
+
+def lrblock_bwd_chained(x, g, A_cat, B, H, sumsq, dY, dx_add=None, act="silu", norm=True, eps=1e-5, d_norm=None,
+                        out=None, ws=None, stream=None):
+    """Backward inside a layer: dx also receives dx_add (the residual path).
+    Returns (dx, dg or None, dA_cat, dB)."""
+    T, d = x.shape
+    G, r, d_out = B.shape
+    desc = lrblock_desc(T, d, r, G, d_out, _dtype_code(x), act, norm, eps, d_norm)
+    if out is None:
+        out = (torch.empty_like(x), _f32((d,), x.device) if norm else None, _f32((d, G * r), x.device),
+               _f32((G, r, d_out), x.device))
+    dx, dg, dA, dB = out
+    ws = _ws(lrblock_workspace_size(desc, True), x.device, ws)
+    _check(lib().boost_lrblock_bwd_chained(ctypes.byref(desc), _ptr(x), _ptr(g) if norm else None, _ptr(A_cat),
+                                           _ptr(B), _ptr(H), _ptr(sumsq) if norm else None, _ptr(dY),
+                                           _ptr(dx_add), _ptr(dx), _ptr(dg), _ptr(dA), _ptr(dB), _ptr(ws),
+                                           ws.numel(), _stream(stream)),
+           "boost_lrblock_bwd_chained")
+    return dx, dg, dA, dB
+
+
+def attn_standin_fwd(qkv, out=None, stream=None):
+    """a = q + k + v for qkv[3,T,d]."""
+    _, T, d = qkv.shape
+    a = out if out is not None else torch.empty((T, d), dtype=qkv.dtype, device=qkv.device)
+    _check(lib().boost_attn_standin_fwd(_dtype_code(qkv), T, d, _ptr(qkv), _ptr(a), _stream(stream)),
+           "boost_attn_standin_fwd")
+    return a
+
+
+def attn_standin_bwd(da, out=None, stream=None):
+    """dqkv[3,T,d] = (da, da, da)."""
+    T, d = da.shape
+    dqkv = out if out is not None else torch.empty((3, T, d), dtype=da.dtype, device=da.device)
+    _check(lib().boost_attn_standin_bwd(_dtype_code(da), T, d, _ptr(da), _ptr(dqkv), _stream(stream)),
+           "boost_attn_standin_bwd")
+    return dqkv
+
+
 # ---------------------------------------------------------------------------
 # MLP
 # ---------------------------------------------------------------------------
@@ -246,6 +312,47 @@ def lrmlp_bwd(x, g, A1_cat, B1, A2, B2, H1, H2, sumsq, dY, act="silu", eps=1e-5,
                                  _ptr(H1), _ptr(H2), _ptr(sumsq), _ptr(dY), _ptr(dx), _ptr(dg), _ptr(dA1),
                                  _ptr(dB1), _ptr(dA2), _ptr(dB2), _ptr(ws), ws.numel(), _stream(stream)),
            "boost_lrmlp_bwd")
+    return dx, dg, dA1, dB1, dA2, dB2
+
+
+def lrmlp_fwd_chained(x, g, A1_cat, B1, A2, B2, residual=None, sumsq_in=None, sumsq_next=False, act="silu",
+                      eps=1e-5, out=None, ws=None, stream=None):
+    """Forward inside a layer (see :func:`lrblock_fwd_chained`). Returns (Y,
+    H1, H2, sumsq or None, sumsq_next or None)."""
+    T, d = x.shape
+    r, ffn = B1.shape[1], B1.shape[2]
+    desc = lrmlp_desc(T, d, r, ffn, _dtype_code(x), act, eps)
+    if out is None:
+        dev = x.device
+        out = (torch.empty_like(x), _f32((T, 2 * r), dev), _f32((T, r), dev),
+               _f32((T,), dev) if sumsq_in is None else None, _f32((T,), dev) if sumsq_next else None)
+    Y, H1, H2, sumsq, snext = out
+    ws = _ws(lrmlp_workspace_size(desc, False), x.device, ws)
+    _check(lib().boost_lrmlp_fwd_chained(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(A1_cat), _ptr(B1), _ptr(A2),
+                                         _ptr(B2), _ptr(residual), _ptr(sumsq_in), _ptr(Y), _ptr(H1), _ptr(H2),
+                                         _ptr(sumsq), _ptr(snext), _ptr(ws), ws.numel(), _stream(stream)),
+           "boost_lrmlp_fwd_chained")
+    return Y, H1, H2, sumsq, snext
+
+
+def lrmlp_bwd_chained(x, g, A1_cat, B1, A2, B2, H1, H2, sumsq, dY, dx_add=None, act="silu", eps=1e-5, out=None,
+                      ws=None, stream=None):
+    """Backward inside a layer: dx also receives dx_add. Returns (dx, dg,
+    dA1_cat, dB1, dA2, dB2)."""
+    T, d = x.shape
+    r, ffn = B1.shape[1], B1.shape[2]
+    desc = lrmlp_desc(T, d, r, ffn, _dtype_code(x), act, eps)
+    if out is None:
+        dev = x.device
+        out = (torch.empty_like(x), _f32((d,), dev), _f32((d, 2 * r), dev), _f32((2, r, ffn), dev),
+               _f32((ffn, r), dev), _f32((r, d), dev))
+    dx, dg, dA1, dB1, dA2, dB2 = out
+    ws = _ws(lrmlp_workspace_size(desc, True), x.device, ws)
+    _check(lib().boost_lrmlp_bwd_chained(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(A1_cat), _ptr(B1), _ptr(A2),
+                                         _ptr(B2), _ptr(H1), _ptr(H2), _ptr(sumsq), _ptr(dY), _ptr(dx_add),
+                                         _ptr(dx), _ptr(dg), _ptr(dA1), _ptr(dB1), _ptr(dA2), _ptr(dB2), _ptr(ws),
+                                         ws.numel(), _stream(stream)),
+           "boost_lrmlp_bwd_chained")
     return dx, dg, dA1, dB1, dA2, dB2
 
 

@@ -113,4 +113,42 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4* __rest
   }
 }
 
+// Attention stand-in (the attention core is not part of the block): a =
+// q + k + v elementwise over qkv[3][n] (fp32 sum, one rounding), and its
+// gradient, dq = dk = dv = da. n is a multiple of 8; 16-byte accesses.
+template <typename T>
+__global__ __launch_bounds__(256) void standin_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ a, int64_t n) {
+  constexpr int VEC = 16 / sizeof(T);
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * VEC; i < n;
+       i += (int64_t)gridDim.x * blockDim.x * VEC) {
+    float q[8], k[8], v[8];
+    if constexpr (VEC == 8) {
+      Vec8<bf16>::load(qkv, i, q);
+      Vec8<bf16>::load(qkv, n + i, k);
+      Vec8<bf16>::load(qkv, 2 * n + i, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] += k[e] + v[e];
+      Vec8<bf16>::store(a, i, q);
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(qkv + i);
+      const float4 y = *reinterpret_cast<const float4*>(qkv + n + i);
+      const float4 z = *reinterpret_cast<const float4*>(qkv + 2 * n + i);
+      *reinterpret_cast<float4*>(a + i) = make_float4(x.x + y.x + z.x, x.y + y.y + z.y, x.z + y.z + z.z,
+                                                      x.w + y.w + z.w);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void standin_bwd_kernel(const T* __restrict__ da, T* __restrict__ dqkv, int64_t n) {
+  constexpr int VEC = 16 / sizeof(T);
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * VEC; i < n;
+       i += (int64_t)gridDim.x * blockDim.x * VEC) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(da + i);
+    *reinterpret_cast<u32x4*>(dqkv + i) = w;
+    *reinterpret_cast<u32x4*>(dqkv + n + i) = w;
+    *reinterpret_cast<u32x4*>(dqkv + 2 * n + i) = w;
+  }
+}
+
 }  // namespace rbo

@@ -418,7 +418,7 @@ int lrblock_check_desc(const boost_lrblock_desc* d) {
 
 struct LrblockPlan {
   Choice down, up, ds, dB, dA, dx;
-  size_t f_AT, f_BT, f_S, fwd_bytes;
+  size_t f_AT, f_BT, f_S, f_part, fwd_bytes;
   size_t b_S, b_dU, b_q, b_dg, b_part, bwd_bytes;
 };
 
@@ -436,6 +436,8 @@ LrblockPlan lrblock_plan(const boost_lrblock_desc* d) {
   p.f_AT = f.take((size_t)(D * G * r * es));
   p.f_BT = f.take((size_t)(G * r * n * es));
   p.f_S = f.take((size_t)(T * G * r * es));
+  // per-tile-column partial row sums of Y^2 (next block's statistic, G = 1)
+  p.f_part = G == 1 ? f.take((size_t)(p.up.tiles_n * T * 4)) : 0;
   p.fwd_bytes = f.total;
   WsLayout b;
   p.b_S = b.take((size_t)(T * G * r * es));
@@ -451,7 +453,8 @@ LrblockPlan lrblock_plan(const boost_lrblock_desc* d) {
 }
 
 int lrblock_fwd_impl(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat, const void* B,
-                     void* Y, float* H, float* sumsq, void* ws, hipStream_t s) {
+                     const void* residual, const float* sumsq_in, void* Y, float* H, float* sumsq,
+                     float* sumsq_next, void* ws, hipStream_t s) {
   const int dt = d->dtype;
   const int64_t T = d->T, D = d->d, r = d->r, G = d->G, n = d->d_out, es = esize(dt);
   const LrblockPlan p = lrblock_plan(d);
@@ -466,21 +469,32 @@ int lrblock_fwd_impl(const boost_lrblock_desc* d, const void* x, const void* g, 
     GemmOps ops{};
     ops.a[0] = opnd(x, D, T, D, es);
     ops.b[0] = opnd(AT, D, G * r, D, es);
-    if (d->norm) {
-      EpiDown<true>::Args ea{H, S, sumsq, G * r, 1.f / (float)d->d_norm, d->eps, d->act};
+    if (d->norm && sumsq_in) {
+      EpiDown<true, true>::Args ea{H, S, sumsq, G * r, 1.f / (float)d->d_norm, d->eps, d->act, sumsq_in};
+      RBO_TRY((gemm<EpiDown<true, true>, true, true, 1>("lrblock_down", dt, p.down, T, G * r, D, 1, ops, ea, s)));
+    } else if (d->norm) {
+      EpiDown<true>::Args ea{H, S, sumsq, G * r, 1.f / (float)d->d_norm, d->eps, d->act, nullptr};
       RBO_TRY((gemm<EpiDown<true>, true, true, 1>("lrblock_down", dt, p.down, T, G * r, D, 1, ops, ea, s)));
     } else {
-      EpiDown<false>::Args ea{H, S, nullptr, G * r, 0.f, 0.f, d->act};
+      EpiDown<false>::Args ea{H, S, nullptr, G * r, 0.f, 0.f, d->act, nullptr};
       RBO_TRY((gemm<EpiDown<false>, true, true, 1>("lrblock_down", dt, p.down, T, G * r, D, 1, ops, ea, s)));
     }
   }
-  // Up, batched over groups: Y_j = S_j @ B_j.
+  // Up, batched over groups: Y_j = S_j @ B_j (+ the residual, and the next
+  // block's row sums of squares, when G = 1).
   {
     GemmOps ops{};
     ops.a[0] = opnd(S, G * r, T, r, es, r);
     ops.b[0] = opnd(BT, r, n, r, es, n * r);
-    EpiStore<false>::Args ea{Y, n, T * n, nullptr};
-    RBO_TRY((gemm<EpiStore<false>, true, true, 1>("lrblock_up", dt, p.up, T, n, r, G, ops, ea, s)));
+    if (residual || sumsq_next) {
+      float* part = sumsq_next ? reinterpret_cast<float*>(at(ws, p.f_part)) : nullptr;
+      EpiUpRes::Args ea{Y, n, residual, part};
+      RBO_TRY((gemm<EpiUpRes, true, true, 1>("lrblock_up", dt, p.up, T, n, r, 1, ops, ea, s)));
+      if (sumsq_next) RBO_TRY(launch_colsum(part, p.up.tiles_n, T, T, sumsq_next, s));
+    } else {
+      EpiStore<false>::Args ea{Y, n, T * n, nullptr};
+      RBO_TRY((gemm<EpiStore<false>, true, true, 1>("lrblock_up", dt, p.up, T, n, r, G, ops, ea, s)));
+    }
   }
   return BOOST_OK;
 }
@@ -499,7 +513,7 @@ int lrblock_bwd_core(int dt, int act, int norm, int64_t T, int64_t D, int64_t r,
                      const float* H, const float* sumsq, const void* dY, void* dx, float* dg, float* dA_cat,
                      float* dB, void* S, bool S_ready, void* dU, float* qpart, float* dgpart, float* partial,
                      const Choice& c_ds, const Choice& c_dB, const Choice& c_dA, const Choice& c_dx,
-                     hipStream_t s, const BwdLabels& L, Side* side) {
+                     hipStream_t s, const BwdLabels& L, Side* side, const void* dadd = nullptr) {
   const int64_t es = esize(dt);
   const float inv = norm ? 1.f / (float)d_norm : 0.f;
   // dS_j = dY_j @ B_j^T, fused: dH, dU = rho dH, S = act(H), row partials q.
@@ -539,7 +553,7 @@ int lrblock_bwd_core(int dt, int act, int norm, int64_t T, int64_t D, int64_t r,
     ops.a[0] = opnd(dU, G * r, T, G * r, es);
     ops.b[0] = opnd(A_cat, G * r, D, G * r, es);
     if (norm) {
-      EpiDX::Args ea{x, g, sumsq, qpart, (int)(G * c_ds.tiles_n), T, inv, eps, dx, dgpart, D};
+      EpiDX::Args ea{x, g, sumsq, qpart, (int)(G * c_ds.tiles_n), T, inv, eps, dx, dgpart, D, dadd};
       RBO_TRY((gemm<EpiDX, true, true, 1>(L.dx, dt, c_dx, T, D, G * r, 1, ops, ea, s)));
       RBO_TRY(launch_colsum(dgpart, c_dx.tiles_m, D, D, dg, s));
     } else {
@@ -573,7 +587,7 @@ int lrmlp_check_desc(const boost_lrmlp_desc* d) {
 struct LrmlpPlan {
   Choice down1, dual, down2, up2;                       // forward
   Choice ds2, dB2, rec, dA2, ds1, dB1, dA1, dx1;        // backward
-  size_t f_A1T, f_B1T, f_A2T, f_B2T, f_S1, f_M, f_S2, fwd_bytes;
+  size_t f_A1T, f_B1T, f_A2T, f_B2T, f_S1, f_M, f_S2, f_part, fwd_bytes;
   size_t b_B1T, b_S2, b_dU2, b_S1, b_M, b_dY, b_dU1, b_q, b_dg, b_part, bwd_bytes;
 };
 
@@ -601,6 +615,7 @@ LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
   p.f_S1 = f.take((size_t)(T * 2 * r * es));
   p.f_M = f.take((size_t)(T * F * es));
   p.f_S2 = f.take((size_t)(T * r * es));
+  p.f_part = f.take((size_t)(p.up2.tiles_n * T * 4));  // next block's statistic partials
   p.fwd_bytes = f.total;
   WsLayout b;
   p.b_B1T = b.take((size_t)(2 * r * F * es));
@@ -710,35 +725,49 @@ int boost_lrblock_workspace_size(const boost_lrblock_desc* d, int is_bwd, size_t
   return BOOST_OK;
 }
 
-int boost_lrblock_fwd(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat, const void* B,
-                      void* Y, float* H, float* sumsq, void* ws, size_t ws_bytes, void* stream) {
+int boost_lrblock_fwd_chained(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat,
+                              const void* B, const void* residual, const float* sumsq_in, void* Y, float* H,
+                              float* sumsq, float* sumsq_next, void* ws, size_t ws_bytes, void* stream) {
   g_detail.clear();
   RBO_TRY(lrblock_check_desc(d));
   const size_t es = esize(d->dtype);
   const size_t T = d->T, D = d->d, r = d->r, G = d->G, n = d->d_out;
+  if ((residual || sumsq_next) && G != 1)
+    return fail(BOOST_ERR_UNSUPPORTED, "residual / sumsq_next need G = 1 (G = %lld)", (long long)G);
+  if (sumsq_in && !d->norm) return fail(BOOST_ERR_INVALID_VALUE, "sumsq_in given but norm = 0");
   const LrblockPlan p = lrblock_plan(d);
   std::vector<Range> rs = {
       {x, T * D * es, "x", false},
       {g, d->norm ? D * es : 0, "g", false},
       {A_cat, D * G * r * es, "A_cat", false},
       {B, G * r * n * es, "B", false},
+      {residual, residual ? T * n * es : 0, "residual", false},
+      {sumsq_in, sumsq_in ? T * 4 : 0, "sumsq_in", false},
       {Y, G * T * n * es, "Y", true},
       {H, T * G * r * 4, "H", true},
-      {sumsq, d->norm ? T * 4 : 0, "sumsq", true},
+      {sumsq, d->norm && (!sumsq_in || sumsq) ? T * 4 : 0, "sumsq", true},
+      {sumsq_next, sumsq_next ? T * 4 : 0, "sumsq_next", true},
       {ws, (ws && p.fwd_bytes <= ws_bytes) ? p.fwd_bytes : 0, "ws", true},
   };
   RBO_TRY(check_ranges(rs));
   RBO_TRY(check_ws(ws, ws_bytes, p.fwd_bytes));
-  return lrblock_fwd_impl(d, x, g, A_cat, B, Y, H, sumsq, ws, as_stream(stream));
+  return lrblock_fwd_impl(d, x, g, A_cat, B, residual, sumsq_in, Y, H, sumsq, sumsq_next, ws, as_stream(stream));
 }
 
-int boost_lrblock_bwd(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat, const void* B,
-                      const float* H, const float* sumsq, const void* dY, void* dx, float* dg, float* dA_cat,
-                      float* dB, void* ws, size_t ws_bytes, void* stream) {
+int boost_lrblock_fwd(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat, const void* B,
+                      void* Y, float* H, float* sumsq, void* ws, size_t ws_bytes, void* stream) {
+  return boost_lrblock_fwd_chained(d, x, g, A_cat, B, nullptr, nullptr, Y, H, sumsq, nullptr, ws, ws_bytes, stream);
+}
+
+int boost_lrblock_bwd_chained(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat,
+                              const void* B, const float* H, const float* sumsq, const void* dY, const void* dx_add,
+                              void* dx, float* dg, float* dA_cat, float* dB, void* ws, size_t ws_bytes,
+                              void* stream) {
   g_detail.clear();
   RBO_TRY(lrblock_check_desc(d));
   const size_t es = esize(d->dtype);
   const size_t T = d->T, D = d->d, r = d->r, G = d->G, n = d->d_out;
+  if (dx_add && !d->norm) return fail(BOOST_ERR_UNSUPPORTED, "dx_add needs norm = 1");
   const LrblockPlan p = lrblock_plan(d);
   std::vector<Range> rs = {
       {x, T * D * es, "x", false},
@@ -748,6 +777,7 @@ int boost_lrblock_bwd(const boost_lrblock_desc* d, const void* x, const void* g,
       {H, T * G * r * 4, "H", false},
       {sumsq, d->norm ? T * 4 : 0, "sumsq", false},
       {dY, G * T * n * es, "dY", false},
+      {dx_add, dx_add ? T * D * es : 0, "dx_add", false},
       {dx, T * D * es, "dx", true},
       {dg, d->norm ? D * 4 : 0, "dg", true},
       {dA_cat, D * G * r * 4, "dA_cat", true},
@@ -763,7 +793,14 @@ int boost_lrblock_bwd(const boost_lrblock_desc* d, const void* x, const void* g,
                           d->norm ? reinterpret_cast<float*>(at(ws, p.b_q)) : nullptr,
                           d->norm ? reinterpret_cast<float*>(at(ws, p.b_dg)) : nullptr,
                           p.b_part ? reinterpret_cast<float*>(at(ws, p.b_part)) : nullptr, p.ds, p.dB, p.dA, p.dx,
-                          as_stream(stream), kLrblockLabels, side);
+                          as_stream(stream), kLrblockLabels, side, dx_add);
+}
+
+int boost_lrblock_bwd(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat, const void* B,
+                      const float* H, const float* sumsq, const void* dY, void* dx, float* dg, float* dA_cat,
+                      float* dB, void* ws, size_t ws_bytes, void* stream) {
+  return boost_lrblock_bwd_chained(d, x, g, A_cat, B, H, sumsq, dY, nullptr, dx, dg, dA_cat, dB, ws, ws_bytes,
+                                   stream);
 }
 
 // ---------------------------------- MLP -----------------------------------
@@ -776,9 +813,10 @@ int boost_lrmlp_workspace_size(const boost_lrmlp_desc* d, int is_bwd, size_t* by
   return BOOST_OK;
 }
 
-int boost_lrmlp_fwd(const boost_lrmlp_desc* d, const void* x, const void* g, const void* A1_cat, const void* B1,
-                    const void* A2, const void* B2, void* Y, float* H1, float* H2, float* sumsq, void* ws,
-                    size_t ws_bytes, void* stream) {
+int boost_lrmlp_fwd_chained(const boost_lrmlp_desc* d, const void* x, const void* g, const void* A1_cat,
+                            const void* B1, const void* A2, const void* B2, const void* residual,
+                            const float* sumsq_in, void* Y, float* H1, float* H2, float* sumsq, float* sumsq_next,
+                            void* ws, size_t ws_bytes, void* stream) {
   g_detail.clear();
   RBO_TRY(lrmlp_check_desc(d));
   const int dt = d->dtype;
@@ -792,10 +830,13 @@ int boost_lrmlp_fwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
       {B1, (size_t)(2 * r * F) * es, "B1", false},
       {A2, (size_t)(F * r) * es, "A2", false},
       {B2, (size_t)(r * D) * es, "B2", false},
+      {residual, residual ? (size_t)(T * D) * es : 0, "residual", false},
+      {sumsq_in, sumsq_in ? (size_t)T * 4 : 0, "sumsq_in", false},
       {Y, (size_t)(T * D) * es, "Y", true},
       {H1, (size_t)(T * 2 * r) * 4, "H1", true},
       {H2, (size_t)(T * r) * 4, "H2", true},
-      {sumsq, (size_t)T * 4, "sumsq", true},
+      {sumsq, (!sumsq_in || sumsq) ? (size_t)T * 4 : 0, "sumsq", true},
+      {sumsq_next, sumsq_next ? (size_t)T * 4 : 0, "sumsq_next", true},
       {ws, (ws && p.fwd_bytes <= ws_bytes) ? p.fwd_bytes : 0, "ws", true},
   };
   RBO_TRY(check_ranges(rs));
@@ -818,8 +859,13 @@ int boost_lrmlp_fwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
     GemmOps ops{};
     ops.a[0] = opnd(x, D, T, D, es);
     ops.b[0] = opnd(A1T, D, 2 * r, D, es);
-    EpiDown<true>::Args ea{H1, S1, sumsq, 2 * r, inv, d->eps, d->act};
-    RBO_TRY((gemm<EpiDown<true>, true, true, 1>("mlp_down1", dt, p.down1, T, 2 * r, D, 1, ops, ea, s)));
+    if (sumsq_in) {
+      EpiDown<true, true>::Args ea{H1, S1, sumsq, 2 * r, inv, d->eps, d->act, sumsq_in};
+      RBO_TRY((gemm<EpiDown<true, true>, true, true, 1>("mlp_down1", dt, p.down1, T, 2 * r, D, 1, ops, ea, s)));
+    } else {
+      EpiDown<true>::Args ea{H1, S1, sumsq, 2 * r, inv, d->eps, d->act, nullptr};
+      RBO_TRY((gemm<EpiDown<true>, true, true, 1>("mlp_down1", dt, p.down1, T, 2 * r, D, 1, ops, ea, s)));
+    }
   }
   {  // M = SiLU(S1_0 @ B1_0) * (S1_1 @ B1_1)
     GemmOps ops{};
@@ -834,23 +880,38 @@ int boost_lrmlp_fwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
     GemmOps ops{};
     ops.a[0] = opnd(M, F, T, F, es);
     ops.b[0] = opnd(A2T, F, r, F, es);
-    EpiDown<false>::Args ea{H2, S2, nullptr, r, 0.f, 0.f, d->act};
+    EpiDown<false>::Args ea{H2, S2, nullptr, r, 0.f, 0.f, d->act, nullptr};
     RBO_TRY((gemm<EpiDown<false>, true, true, 1>("mlp_down2", dt, p.down2, T, r, F, 1, ops, ea, s)));
   }
   {  // Y = S2 @ B2
     GemmOps ops{};
     ops.a[0] = opnd(S2, r, T, r, es);
     ops.b[0] = opnd(B2T, r, D, r, es);
-    EpiStore<false>::Args ea{Y, D, 0, nullptr};
-    RBO_TRY((gemm<EpiStore<false>, true, true, 1>("mlp_up2", dt, p.up2, T, D, r, 1, ops, ea, s)));
+    if (residual || sumsq_next) {
+      float* part = sumsq_next ? reinterpret_cast<float*>(at(ws, p.f_part)) : nullptr;
+      EpiUpRes::Args ea{Y, D, residual, part};
+      RBO_TRY((gemm<EpiUpRes, true, true, 1>("mlp_up2", dt, p.up2, T, D, r, 1, ops, ea, s)));
+      if (sumsq_next) RBO_TRY(launch_colsum(part, p.up2.tiles_n, T, T, sumsq_next, s));
+    } else {
+      EpiStore<false>::Args ea{Y, D, 0, nullptr};
+      RBO_TRY((gemm<EpiStore<false>, true, true, 1>("mlp_up2", dt, p.up2, T, D, r, 1, ops, ea, s)));
+    }
   }
   return BOOST_OK;
 }
 
-int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, const void* A1_cat, const void* B1,
-                    const void* A2, const void* B2, const float* H1, const float* H2, const float* sumsq,
-                    const void* dY, void* dx, float* dg, float* dA1_cat, float* dB1, float* dA2, float* dB2,
-                    void* ws, size_t ws_bytes, void* stream) {
+int boost_lrmlp_fwd(const boost_lrmlp_desc* d, const void* x, const void* g, const void* A1_cat, const void* B1,
+                    const void* A2, const void* B2, void* Y, float* H1, float* H2, float* sumsq, void* ws,
+                    size_t ws_bytes, void* stream) {
+  return boost_lrmlp_fwd_chained(d, x, g, A1_cat, B1, A2, B2, nullptr, nullptr, Y, H1, H2, sumsq, nullptr, ws,
+                                 ws_bytes, stream);
+}
+
+int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void* g, const void* A1_cat,
+                            const void* B1, const void* A2, const void* B2, const float* H1, const float* H2,
+                            const float* sumsq, const void* dY, const void* dx_add, void* dx, float* dg,
+                            float* dA1_cat, float* dB1, float* dA2, float* dB2, void* ws, size_t ws_bytes,
+                            void* stream) {
   g_detail.clear();
   RBO_TRY(lrmlp_check_desc(d));
   const int dt = d->dtype;
@@ -868,6 +929,7 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
       {H2, (size_t)(T * r) * 4, "H2", false},
       {sumsq, (size_t)T * 4, "sumsq", false},
       {dY, (size_t)(T * D) * es, "dY", false},
+      {dx_add, dx_add ? (size_t)(T * D) * es : 0, "dx_add", false},
       {dx, (size_t)(T * D) * es, "dx", true},
       {dg, (size_t)D * 4, "dg", true},
       {dA1_cat, (size_t)(D * 2 * r) * 4, "dA1_cat", true},
@@ -931,7 +993,15 @@ int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, con
   // the side stream back into the caller's before returning.
   return lrblock_bwd_core(dt, d->act, 1, T, D, r, 2, F, d->eps, D, x, g, A1_cat, B1, H1, sumsq, dYgu, dx, dg,
                           dA1_cat, dB1, S1, true, dU1, q, dgp, part, p.ds1, p.dB1, p.dA1, p.dx1, s, kMlp1Labels,
-                          side);
+                          side, dx_add);
+}
+
+int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, const void* A1_cat, const void* B1,
+                    const void* A2, const void* B2, const float* H1, const float* H2, const float* sumsq,
+                    const void* dY, void* dx, float* dg, float* dA1_cat, float* dB1, float* dA2, float* dB2,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return boost_lrmlp_bwd_chained(d, x, g, A1_cat, B1, A2, B2, H1, H2, sumsq, dY, nullptr, dx, dg, dA1_cat, dB1,
+                                 dA2, dB2, ws, ws_bytes, stream);
 }
 
 // --------------------------- tensor-parallel share -------------------------
@@ -1062,6 +1132,52 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
 }
 
 // ------------------------------- profiler ---------------------------------
+// ---------------------------- attention stand-in ---------------------------
+static int standin_check(int dtype, int64_t T, int64_t d) {
+  RBO_TRY(check_dtype(dtype));
+  RBO_TRY(check_T(T));
+  RBO_TRY(check_dim64(d, "d"));
+  return BOOST_OK;
+}
+
+int boost_attn_standin_fwd(int dtype, int64_t T, int64_t d, const void* qkv, void* a, void* stream) {
+  g_detail.clear();
+  RBO_TRY(standin_check(dtype, T, d));
+  const size_t n = (size_t)(T * d), es = esize(dtype);
+  std::vector<Range> rs = {{qkv, 3 * n * es, "qkv", false}, {a, n * es, "a", true}};
+  RBO_TRY(check_ranges(rs));
+  hipStream_t s = as_stream(stream);
+  const int grid = grid_for((int64_t)n, 8);
+  prof_begin("attn_standin", s);
+  if (dtype == BOOST_DT_BF16)
+    hipLaunchKernelGGL(standin_fwd_kernel<bf16>, dim3(grid), dim3(256), 0, s, static_cast<const bf16*>(qkv),
+                       static_cast<bf16*>(a), (int64_t)n);
+  else
+    hipLaunchKernelGGL(standin_fwd_kernel<float>, dim3(grid), dim3(256), 0, s, static_cast<const float*>(qkv),
+                       static_cast<float*>(a), (int64_t)n);
+  prof_end(s);
+  return check_launch("attn_standin");
+}
+
+int boost_attn_standin_bwd(int dtype, int64_t T, int64_t d, const void* da, void* dqkv, void* stream) {
+  g_detail.clear();
+  RBO_TRY(standin_check(dtype, T, d));
+  const size_t n = (size_t)(T * d), es = esize(dtype);
+  std::vector<Range> rs = {{da, n * es, "da", false}, {dqkv, 3 * n * es, "dqkv", true}};
+  RBO_TRY(check_ranges(rs));
+  hipStream_t s = as_stream(stream);
+  const int grid = grid_for((int64_t)n, 16 / (int)es);
+  prof_begin("attn_standin_bwd", s);
+  if (dtype == BOOST_DT_BF16)
+    hipLaunchKernelGGL(standin_bwd_kernel<bf16>, dim3(grid), dim3(256), 0, s, static_cast<const bf16*>(da),
+                       static_cast<bf16*>(dqkv), (int64_t)n);
+  else
+    hipLaunchKernelGGL(standin_bwd_kernel<float>, dim3(grid), dim3(256), 0, s, static_cast<const float*>(da),
+                       static_cast<float*>(dqkv), (int64_t)n);
+  prof_end(s);
+  return check_launch("attn_standin_bwd");
+}
+
 int boost_profiler_enable(const char* name_filter, int max_records) {
   g_detail.clear();
   boost_profiler_disable();

@@ -122,24 +122,31 @@ struct EpiStore : EpiBase {
 // H = rho * acc (fp32, saved), S = act(H) (dtype, operand of the up
 // products), sumsq from the A loader's row statistics (tile column 0 writes).
 // ---------------------------------------------------------------------------
-template <bool NORM>
+template <bool NORM, bool GIVEN = false>
 struct EpiDown : EpiBase {
-  static constexpr bool kRowSumsq = NORM;
+  // GIVEN: the row sums of squares come from the producer of x (sumsq_in)
+  // instead of being taken from the A fragments here.
+  static constexpr bool kRowSumsq = NORM && !GIVEN;
   struct Args {
     float* H;
     void* S;
-    float* sumsq;
-    int64_t ld;  // columns of H and S
+    float* sumsq;           // out (may be null when GIVEN)
+    int64_t ld;             // columns of H and S
     float inv_dnorm, eps;
     int act;
+    const float* sumsq_in;  // GIVEN only
   };
   template <class C>
   static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
     if constexpr (NORM) {
-      // rowv holds the row sums of squares; publish them and turn them into rho.
+      // rowv holds (or receives) the row sums of squares; publish them and
+      // turn them into rho.
       for (int r = c.t; r < C::BM; r += C::NT) {
-        const float ss = c.rowv[r];
-        if (c.tn == 0 && c.split == 0 && c.m0 + r < c.M) a.sumsq[c.m0 + r] = ss;
+        const bool in = c.m0 + r < c.M;
+        float ss;
+        if constexpr (GIVEN) ss = in ? a.sumsq_in[c.m0 + r] : 0.f;
+        else ss = c.rowv[r];
+        if (a.sumsq && c.tn == 0 && c.split == 0 && in) a.sumsq[c.m0 + r] = ss;
         c.rowv[r] = rms_scale(ss, a.inv_dnorm, a.eps);
       }
     }
@@ -160,6 +167,59 @@ struct EpiDown : EpiBase {
     const int64_t o = (int64_t)row * a.ld + col;
     Vec8<float>::store(a.H, o, h);
     Vec8<T>::store(a.S, o, sv);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Up projection into a residual stream: out = res + acc (dtype), and per-row
+// partial sums over this tile's columns of out^2, taken from the stored
+// (rounded) values: the statistic the next block's Online-RMSNorm needs,
+// emitted by the kernel that produces its input. One row of partials per
+// tile column (part[tn][row]); null part skips them.
+// ---------------------------------------------------------------------------
+struct EpiUpRes : EpiBase {
+  static constexpr bool kRowSum = true;
+  struct Pre {
+    float r[8];
+  };
+  struct Args {
+    void* out;
+    int64_t ldo;
+    const void* res;  // [M, ldo] dtype, or null (no residual)
+    float* part;      // [tiles_n][M] fp32 or null
+  };
+  template <class C>
+  static __device__ __forceinline__ void pre(const TileCtx& c, const Args& a, int lr, int lc, Pre& pf) {
+    typedef typename C::T T;
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    if (a.res) {
+      Vec8<T>::load(a.res, (int64_t)row * a.ldo + col, pf.r);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf.r[e] = 0.f;
+    }
+  }
+  template <class C>
+  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
+                                               const float (&v)[C::NACC][8], const Pre& pf, float& rowc,
+                                               float (&)[8]) {
+    typedef typename C::T T;
+    const int row = c.m0 + lr, col = c.n0 + lc;
+    if (row >= c.M || col >= c.N) return;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] = Elem<T>::round(pf.r[e] + v[0][e]);
+      rowc += o[e] * o[e];
+    }
+    Vec8<T>::store(a.out, (int64_t)row * a.ldo + col, o);
+  }
+  template <class C>
+  static __device__ __forceinline__ void rows_done(const TileCtx& c, const Args& a, const float* sums) {
+    if (!a.part) return;
+    for (int r = c.t; r < C::BM; r += C::NT)
+      if (c.m0 + r < c.M) a.part[(int64_t)c.tn * c.M + c.m0 + r] = sums[r];
   }
 };
 
@@ -261,7 +321,7 @@ struct EpiDS : EpiBase {
 struct EpiDX : EpiBase {
   static constexpr bool kColSum = true;
   struct Pre {
-    float x[8], g[8];
+    float x[8], g[8], add[8];
   };
   struct Args {
     const void* x;
@@ -272,8 +332,9 @@ struct EpiDX : EpiBase {
     int64_t qstride;
     float inv_dnorm, eps;
     void* dx;
-    float* dgpart;  // [tiles_m][ld]
-    int64_t ld;     // d
+    float* dgpart;     // [tiles_m][ld]
+    int64_t ld;        // d
+    const void* dadd;  // [T, d] dtype gradient added to dx (residual path), or null
   };
   template <class C>
   static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
@@ -296,6 +357,7 @@ struct EpiDX : EpiBase {
     if (row >= c.M || col >= c.N) return;
     Vec8<T>::load(a.x, (int64_t)row * a.ld + col, pf.x);
     Vec8<T>::load(a.g, col, pf.g);
+    if (a.dadd) Vec8<T>::load(a.dadd, (int64_t)row * a.ld + col, pf.add);
   }
   template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
@@ -310,7 +372,7 @@ struct EpiDX : EpiBase {
     const float (&gv)[8] = pf.g;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      dx[e] = gv[e] * v[0][e] - coef * xv[e];
+      dx[e] = gv[e] * v[0][e] - coef * xv[e] + (a.dadd ? pf.add[e] : 0.f);
       colc[e] += xv[e] * v[0][e];
     }
     Vec8<T>::store(a.dx, o, dx);

@@ -97,6 +97,8 @@ template <> struct Elem<bf16> {
   static __device__ __forceinline__ float load(const void* p, int64_t i) {
     return to_f32(static_cast<const uint16_t*>(p)[i]);
   }
+  // The value a store of v would leave in memory (round to nearest even).
+  static __device__ __forceinline__ float round(float v) { return static_cast<float>(static_cast<bf16>(v)); }
 };
 template <> struct Elem<float> {
   static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
@@ -105,6 +107,7 @@ template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
   }
+  static __device__ __forceinline__ float round(float v) { return v; }
 };
 
 // ---------------------------------------------------------------------------

@@ -183,3 +183,40 @@ def test_workspace_sizes_scale_with_tokens(B):
          for T in (2048, 4096, 8192)}
     assert w[8192] - w[4096] == pytest.approx(2 * (w[4096] - w[2048]), rel=0.02)
     assert w[2048] > 0
+
+
+def test_chained_entry_points_validate_their_extra_arguments(B):
+    E_INV, E_UNS, E_ALI, E_WS = 1, 2, 4, 5
+    L = B.lib()
+    f = Fake()
+    T, d, r = 300, 256, 64
+
+    def fwd(desc, residual=True, sumsq_in=False, sumsq=True, snext=True, ws_bytes=1):
+        G, n = desc.G, desc.d_out
+        x, g, A, Bw = f(T * d * 2), f(d * 2), f(d * G * r * 2), f(G * r * n * 2)
+        return L.boost_lrblock_fwd_chained(ctypes.byref(desc), x, g, A, Bw, f(T * n * 2) if residual else None,
+                                           f(T * 4) if sumsq_in else None, f(G * T * n * 2), f(T * G * r * 4),
+                                           f(T * 4) if sumsq else None, f(T * 4) if snext else None, f(1 << 20),
+                                           ws_bytes, None)
+
+    # residual and the next statistic need G = 1
+    assert fwd(desc_(B, G=3, d_out=256)) == E_UNS
+    assert fwd(desc_(B, G=3, d_out=256), residual=False) == E_UNS
+    # with G = 1 every extra argument is accepted; only the tiny workspace fails
+    assert fwd(desc_(B, G=1, d_out=256)) == E_WS
+    assert fwd(desc_(B, G=1, d_out=256), sumsq_in=True, sumsq=False) == E_WS
+    # a producer statistic makes no sense without the norm
+    assert fwd(desc_(B, G=1, d_out=256, norm=False), sumsq_in=True, sumsq=False) == E_INV
+    # the residual path of the backward is only fused into the normalised dx
+    dsc = desc_(B, G=1, d_out=256, norm=False)
+    args = [f(1 << 20) for _ in range(12)]
+    assert L.boost_lrblock_bwd_chained(ctypes.byref(dsc), *args, f(1 << 20), 1, None) == E_UNS
+    # stand-in: dims and overlap
+    qkv, a = f(3 * T * d * 2), f(T * d * 2)
+    assert L.boost_attn_standin_fwd(B.DT_BF16, T, 100, qkv, a, None) == E_UNS
+    assert L.boost_attn_standin_fwd(B.DT_BF16, T, d, qkv, qkv, None) == E_ALI
+    assert L.boost_attn_standin_bwd(B.DT_BF16, T, d, None, qkv, None) == E_INV
+    # MLP chained forward: extra arguments accepted, then the workspace check
+    m = B.lrmlp_desc(128, 256, 64, 192, B.DT_BF16)
+    margs = [f(1 << 20) for _ in range(6)] + [f(1 << 20), f(1 << 20)] + [f(1 << 20) for _ in range(4)] + [f(1 << 20)]
+    assert L.boost_lrmlp_fwd_chained(ctypes.byref(m), *margs, f(1 << 20), 1, None) == E_WS
