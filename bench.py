@@ -34,6 +34,7 @@ from rank_bottleneck_online_amd import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "low-rank block fwd+bwd TFLOP/s (% bf16 MFMA peak) + tokens/s, 7B shape"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -73,6 +74,26 @@ def mlp_kernel_flops(T, d, r, ffn):
     }
 
 
+def mlp_kernel_bytes(T, d, r, ffn):
+    """Algorithmic HBM bytes per launch of the MLP step's kernels: each input
+    read once, each output written once (bf16 2 B, fp32 4 B)."""
+    b, f = 2, 4
+    return {
+        "mlp_down1": T * d * b + d * 2 * r * b + T * 2 * r * (f + b) + T * f,
+        "mlp_up1_swiglu": T * 2 * r * b + 2 * r * ffn * b + T * ffn * b,
+        "mlp_down2": T * ffn * b + ffn * r * b + T * r * (f + b),
+        "mlp_up2": T * r * b + r * d * b + T * d * b,
+        "mlp_ds2": T * d * b + r * d * b + T * r * f + 2 * T * r * b,
+        "mlp_dB2": T * r * b + T * d * b + r * d * f,
+        "mlp_recompute_swiglu_bwd": T * 2 * r * b + 2 * r * ffn * b + T * r * b + ffn * r * b + 3 * T * ffn * b,
+        "mlp_dA2": T * ffn * b + T * r * b + ffn * r * f,
+        "mlp1_ds": 2 * T * ffn * b + 2 * r * ffn * b + T * 2 * r * f + T * 2 * r * b,
+        "mlp1_dB": T * 2 * r * b + 2 * T * ffn * b + 2 * r * ffn * f,
+        "mlp1_dA": T * d * b + T * 2 * r * b + d * 2 * r * f,
+        "mlp1_dx": T * 2 * r * b + d * 2 * r * b + 2 * T * d * b,
+    }
+
+
 def lrblock_kernel_flops(T, d, r, G, n, bwd=True):
     f = {"lrblock_down": 2 * T * d * G * r, "lrblock_up": 2 * G * T * r * n}
     if bwd:
@@ -85,7 +106,7 @@ def recompute_flops(kind, w) -> float:
     """Flops of the prescribed recompute in one step (the gate/up re-forward
     of each MLP, u of the BTP share)."""
     mlp = 2 * 2 * w["T"] * w["r"] * w.get("ffn", 0)
-    if kind in ("lrmlp", "layerset"):
+    if kind in ("lrmlp", "layerset", "layer"):
         return float(mlp)
     if kind == "btp":
         return float(2 * w["T"] * w["r"] * (w["d_global"] // w["P"]))
@@ -149,6 +170,7 @@ class Workload:
             self.fwd, self.bwd_fn = fwd, bwd
             self.tokens = T
             self.kflops = mlp_kernel_flops(T, d, r, ffn)
+            self.kbytes = mlp_kernel_bytes(T, d, r, ffn)
             self.shape = dict(T=T, d=d, r=r, ffn=ffn)
         elif self.kind == "lrblock":
             T, d, r, G, n = w["T"], w["d"], w["r"], w["G"], w["d_out"]
@@ -243,6 +265,62 @@ class Workload:
             # per-launch flops, so only the MLP kernels get a roofline here.
             self.kflops = mlp_kernel_flops(T, d, r, ffn)
             self.shape = dict(T=T, d=d, r=r, ffn=ffn)
+        elif self.kind == "layer":
+            T, d, r, ffn = w["T"], w["d"], w["r"], w["ffn"]
+            inp = synth.layer_inputs(T, d, r, ffn, dtype=self.dtype, seed=0)
+            x, dh3 = self.dev(inp["x"]), self.dev(inp["dh3"])
+            q = {k: self.dev(v) for k, v in inp["qkv"].items()}
+            o = {k: self.dev(v) for k, v in inp["o"].items()}
+            m = {k: self.dev(v) for k, v in inp["mlp"].items()}
+            dq = B.lrblock_desc(T, d, r, 3, d, dt)
+            do = B.lrblock_desc(T, d, r, 1, d, dt, norm=False)
+            dm = B.lrmlp_desc(T, d, r, ffn, dt)
+            sizes = [B.lrblock_workspace_size(dq, 0), B.lrblock_workspace_size(dq, 1),
+                     B.lrblock_workspace_size(do, 0), B.lrblock_workspace_size(do, 1),
+                     B.lrmlp_workspace_size(dm, 0), B.lrmlp_workspace_size(dm, 1)]
+            ws = torch.empty(max(sizes), dtype=torch.uint8, device="cuda")
+            act = "silu"
+            ma = [m[k] for k in ("g", "A1_cat", "B1", "A2", "B2")]
+            # outputs and saved tensors, allocated once
+            qf = B.lrblock_fwd_chained(x, q["g"], q["A_cat"], q["B"], act=act, ws=ws)
+            a = B.attn_standin_fwd(qf[0])
+            of = B.lrblock_fwd_chained(a, None, o["A_cat"], o["B"], residual=x, sumsq_next=True, act=act,
+                                       norm=False, ws=ws)
+            h2 = of[0][0]
+            mf = B.lrmlp_fwd_chained(h2, *ma, residual=h2, sumsq_in=of[3], sumsq_next=True, act=act, ws=ws)
+            mb = B.lrmlp_bwd_chained(h2, *ma, mf[1], mf[2], of[3], dh3, dx_add=dh3, act=act, ws=ws)
+            ob = B.lrblock_bwd_chained(a, None, o["A_cat"], o["B"], of[1], None, mb[0][None], act=act, norm=False,
+                                       ws=ws)
+            dqkv = B.attn_standin_bwd(ob[0])
+            qb = B.lrblock_bwd_chained(x, q["g"], q["A_cat"], q["B"], qf[1], qf[2], dqkv, dx_add=mb[0], act=act,
+                                       ws=ws)
+
+            def fwd():
+                B.lrblock_fwd_chained(x, q["g"], q["A_cat"], q["B"], act=act, out=qf, ws=ws)
+                B.attn_standin_fwd(qf[0], out=a)
+                B.lrblock_fwd_chained(a, None, o["A_cat"], o["B"], residual=x, sumsq_next=True, act=act,
+                                      norm=False, out=of, ws=ws)
+                B.lrmlp_fwd_chained(h2, *ma, residual=h2, sumsq_in=of[3], sumsq_next=True, act=act, out=mf,
+                                    ws=ws)
+
+            def bwd():
+                B.lrmlp_bwd_chained(h2, *ma, mf[1], mf[2], of[3], dh3, dx_add=dh3, act=act, out=mb, ws=ws)
+                B.lrblock_bwd_chained(a, None, o["A_cat"], o["B"], of[1], None, mb[0][None], act=act, norm=False,
+                                      out=ob, ws=ws)
+                B.attn_standin_bwd(ob[0], out=dqkv)
+                B.lrblock_bwd_chained(x, q["g"], q["A_cat"], q["B"], qf[1], qf[2], dqkv, dx_add=mb[0], act=act,
+                                      out=qb, ws=ws)
+
+            self.fwd, self.bwd_fn = fwd, bwd
+            self.act = act
+            self.tokens = T
+            # the QKV and O launches share the lrblock_* labels, so only the
+            # MLP kernels get a per-kernel roofline here
+            self.kflops = mlp_kernel_flops(T, d, r, ffn)
+            self.kbytes = mlp_kernel_bytes(T, d, r, ffn)
+            self.shape = dict(T=T, d=d, r=r, ffn=ffn)
+        if not hasattr(self, "kbytes"):
+            self.kbytes = {}
         self.flops = self.step_flops()
         self.model_flops = self.step_flops(model_only=True)
 
@@ -267,6 +345,7 @@ class Workload:
         if self.kind == "btp":
             return tot(btp_kernel_flops(w["T"], w["r"], w["d_global"] // w["P"])) - sub
         T, d, r, ffn = w["T"], w["d"], w["r"], w["ffn"]
+        # layer set and chained layer: the same products (QKV, O, MLP)
         return (tot(lrblock_kernel_flops(T, d, r, 3, d)) + tot(lrblock_kernel_flops(T, d, r, 1, d)) +
                 tot(mlp_kernel_flops(T, d, r, ffn))) - sub
 
@@ -312,6 +391,16 @@ def cpu_baseline(name, target_s):
             oracle.btp_share_backward(*a, sh["dp"], sh["ds"])
             dt = time.perf_counter() - t0
             return dt, float(sum(btp_kernel_flops(Ts, w["r"], w["d_global"] // w["P"]).values()))
+        if w["kind"] == "layer":
+            inp = synth.layer_inputs(Ts, w["d"], w["r"], w["ffn"], dtype=w["dtype"], seed=0)
+            t0 = time.perf_counter()
+            oracle.layer_backward(inp["x"], inp["qkv"], inp["o"], inp["mlp"], inp["dh3"], "silu",
+                                  store=oracle.round_to_bf16)
+            dt = time.perf_counter() - t0
+            T, d, r, ffn = Ts, w["d"], w["r"], w["ffn"]
+            fl = (sum(lrblock_kernel_flops(T, d, r, 3, d).values()) +
+                  sum(lrblock_kernel_flops(T, d, r, 1, d).values()) + sum(mlp_kernel_flops(T, d, r, ffn).values()))
+            return dt, float(fl)
         inp = synth.layerset_inputs(Ts, w["d"], w["r"], w["ffn"], dtype=w["dtype"], seed=0)
         t0 = time.perf_counter()
         q, o, m = inp["qkv"], inp["o"], inp["mlp"]
@@ -610,6 +699,14 @@ def main():
         if kf and kms > 0:
             kernels[k]["tflops"] = round(kf / (kms * 1e-3) / 1e12, 1)
             kernels[k]["frac"] = round(kf / (kms * 1e-3) / 1e12 / peak, 4)
+            kb = wl.kbytes.get(k)
+            if kb:
+                # roofline time max(F/peak, B/HBM) over the measured time
+                t_mfma, t_hbm = kf / (peak * 1e12), kb / (PEAK_HBM_GBS * 1e9)
+                kernels[k]["alg_gb"] = round(kb / 1e9, 3)
+                kernels[k]["alg_gbs"] = round(kb / (kms * 1e-3) / 1e9, 1)
+                kernels[k]["roofline_bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
+                kernels[k]["roofline_frac"] = round(max(t_mfma, t_hbm) / (kms * 1e-3), 4)
 
     cpu = None
     if args.cpu_baseline == "on":
