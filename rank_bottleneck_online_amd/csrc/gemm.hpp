@@ -182,8 +182,8 @@ struct Cfg {
   static constexpr int PIPE_BYTES = NSTAGE * STAGE_BYTES;
   // Epilogue staging: each wave writes 32 accumulator rows at a time (per
   // accumulator) into a private fp32 buffer with a row stride padded by 8
-  // floats (the two half-waves of the MFMA layout then hit disjoint banks),
-  // reusing the pipeline LDS.
+  // floats (the two half-waves of the MFMA layout then hit disjoint banks;
+  // odd rows are column-swizzled for the read-back), reusing the pipeline LDS.
   static constexpr int EPI_STR = WTN + 8;
   // Accumulator rows staged per round: 32 (one MFMA block row), or 16 with
   // three accumulators so the staging still fits next to the pipeline.
@@ -439,7 +439,11 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
         static_for<0, C::FN>([&](auto j) {
           static_for<h * (16 / ROUNDS), (h + 1) * (16 / ROUNDS)>([&](auto v) {
             constexpr int r0 = (v >> 2) * 8 + (v & 3) - h * ER;
-            scr[p * SUB + (r0 + (c.lane >> 5) * 4) * STR + j * 32 + (c.lane & 31)] = acc[p][i][j][v()];
+            // Odd rows hold their 4-column groups swapped in pairs (column
+            // ^ 4), so the read-back of two neighbouring rows hits disjoint
+            // banks; the row parity is that of v.
+            scr[p * SUB + (r0 + (c.lane >> 5) * 4) * STR + ((j * 32 + (c.lane & 31)) ^ (4 * (v & 1)))] =
+                acc[p][i][j][v()];
           });
         });
       });
@@ -449,10 +453,11 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
         const int lr = c.wm * C::WTM + i * 32 + h * ER + r;
         const int lc = c.wn * C::WTN + c8 * 8;
         float vals[C::NACC][8];
+        const int swz = 4 * (r & 1);
         static_for<0, C::NACC>([&](auto p) {
           const float* src = scr + p * SUB + r * STR + c8 * 8;
-          const float4 a = *reinterpret_cast<const float4*>(src);
-          const float4 b = *reinterpret_cast<const float4*>(src + 4);
+          const float4 a = *reinterpret_cast<const float4*>(src + swz);
+          const float4 b = *reinterpret_cast<const float4*>(src + (swz ^ 4));
           vals[p][0] = a.x; vals[p][1] = a.y; vals[p][2] = a.z; vals[p][3] = a.w;
           vals[p][4] = b.x; vals[p][5] = b.y; vals[p][6] = b.z; vals[p][7] = b.w;
         });
@@ -546,100 +551,127 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) ss[i] = 0.f;
 
+  // Buffer resources of every operand pair, rebased on this tile so 32-bit
+  // buffer offsets suffice.
+  __amdgpu_buffer_rsrc_t ra[C::NACC], rb[C::NACC];
+  int64_t lda_b[C::NACC], ldb_b[C::NACC];
   static_for<0, C::NACC>([&](auto p) {
     const Operand& A = ops.a[p];
     const Operand& B = ops.b[p];
-    // Rebase each operand on this tile so 32-bit buffer offsets suffice.
     const int64_t a_off = (int64_t)bidx * A.batch_stride * C::ES +
                           (C::AKC ? (int64_t)m0 * A.ld * C::ES : (int64_t)m0 * C::ES);
     const int64_t b_off = (int64_t)bidx * B.batch_stride * C::ES +
                           (C::BKC ? (int64_t)n0 * B.ld * C::ES : (int64_t)n0 * C::ES);
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(static_cast<const char*>(A.ptr) + a_off, A.extent - ((int64_t)m0 * (C::AKC ? A.ld : 1) * C::ES));
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(static_cast<const char*>(B.ptr) + b_off, B.extent - ((int64_t)n0 * (C::BKC ? B.ld : 1) * C::ES));
-    const int64_t lda_b = A.ld * C::ES, ldb_b = B.ld * C::ES;
-    const int kl = (lane >> 5) * MF::KL;
+    ra[p] = make_rsrc(static_cast<const char*>(A.ptr) + a_off,
+                      A.extent - ((int64_t)m0 * (C::AKC ? A.ld : 1) * C::ES));
+    rb[p] = make_rsrc(static_cast<const char*>(B.ptr) + b_off,
+                      B.extent - ((int64_t)n0 * (C::BKC ? B.ld : 1) * C::ES));
+    lda_b[p] = A.ld * C::ES;
+    ldb_b[p] = B.ld * C::ES;
+  });
+  const int kl = (lane >> 5) * MF::KL;
 
-    // Loaders and fragment readers of this operand layout pair.
-    typedef std::conditional_t<C::AKC, DirectLoader<C, C::BM>, DirectLoaderMN<C, C::BM>> DA;
-    typedef std::conditional_t<C::BKC, DirectLoader<C, C::BN>, DirectLoaderMN<C, C::BN>> DB;
-    auto frag_a = [&](const char* As, int i, int k) {
-      if constexpr (C::AKC) return MF::read(As, wm * C::WTM + i * 32 + (lane & 31), k + kl);
-      else return MnFrag<C, C::BM * C::ES>::read(As, wm * C::WTM + i * 32, k, lane);
-    };
-    auto frag_b = [&](const char* Bs, int j, int k) {
-      if constexpr (C::BKC) return MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), k + kl);
-      else return MnFrag<C, C::BN * C::ES>::read(Bs, wn * C::WTN + j * 32, k, lane);
-    };
+  // Loaders and fragment readers of this operand layout pair.
+  typedef std::conditional_t<C::AKC, DirectLoader<C, C::BM>, DirectLoaderMN<C, C::BM>> DA;
+  typedef std::conditional_t<C::BKC, DirectLoader<C, C::BN>, DirectLoaderMN<C, C::BN>> DB;
+  auto frag_a = [&](const char* As, int i, int k) {
+    if constexpr (C::AKC) return MF::read(As, wm * C::WTM + i * 32 + (lane & 31), k + kl);
+    else return MnFrag<C, C::BM * C::ES>::read(As, wm * C::WTM + i * 32, k, lane);
+  };
+  auto frag_b = [&](const char* Bs, int j, int k) {
+    if constexpr (C::BKC) return MF::read(Bs, wn * C::WTN + j * 32 + (lane & 31), k + kl);
+    else return MnFrag<C, C::BN * C::ES>::read(Bs, wn * C::WTN + j * 32, k, lane);
+  };
 
-    // MFMAs of one LDS stage. stage_work(kk) issues the NV(kk) global->LDS
-    // load instructions of a later slab (sub-steps 0 and 1), interleaved one
-    // by one with that sub-step's MFMAs.
-    auto compute = [&](const char* As, const char* Bs, auto nv_tag, auto&& stage_work) {
-      typedef decltype(nv_tag) NV;
-      typename MF::Frag fa[2][C::FM], fb[2][C::FN];
-      static_for<0, C::FM>([&](auto i) { fa[0][i] = frag_a(As, i, 0); });
-      static_for<0, C::FN>([&](auto j) { fb[0][j] = frag_b(Bs, j, 0); });
-      // LDS read instructions per sub-step (a bf16 MN-major fragment takes two)
-      constexpr int NR = C::FM * (C::AKC || C::ES == 4 ? 1 : 2) + C::FN * (C::BKC || C::ES == 4 ? 1 : 2);
-      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // sub-step 0's reads lead
-      static_for<0, KK>([&](auto kk) {
-        constexpr int cur = kk & 1, nxt = cur ^ 1;
-        constexpr int nv = NV::at(kk);
-        if constexpr (kk + 1 < KK) {
-          const int k = (kk + 1) * MF::KI;
-          static_for<0, C::FM>([&](auto i) { fa[nxt][i] = frag_a(As, i, k); });
-          static_for<0, C::FN>([&](auto j) { fb[nxt][j] = frag_b(Bs, j, k); });
-        }
-        static_for<0, C::FM>([&](auto i) {
-          static_for<0, C::FN>([&](auto j) { acc[p][i][j] = MF::mma(fa[cur][i], fb[cur][j], acc[p][i][j]); });
-        });
-        if constexpr (nv > 0) stage_work(kk);
-        // Issue order: every fragment read of sub-step kk+1, then the MFMAs of
-        // sub-step kk (with the slab loads, if any, one after every few
-        // MFMAs), so the reads have a whole sub-step of MFMAs to land (left
-        // alone, the scheduler issues each read just before its use).
-        if constexpr (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-        if constexpr (nv > 0) {
-          constexpr int NM = C::FM * C::FN;
-          static_for<0, nv>([&](auto v) {
-            constexpr int m = (NM * (v + 1)) / nv - (NM * v) / nv;  // MFMAs after load v
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
-          });
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
-        }
-        // The WN waves of a wave row hold the same A fragments; each takes
-        // every WN-th sub-step (a wave-uniform branch), so the sums cost each
-        // wave 1/WN of the dot products.
-        if constexpr (RSS) {
-          if (wn == kk % C::WN) static_for<0, C::FM>([&](auto i) { ss[i] = frag_sumsq(fa[cur][i], ss[i]); });
-        }
+  // MFMAs of one LDS stage into accumulator p. stage_work(kk) issues the
+  // NV(kk) global->LDS load instructions of a later slab, interleaved one by
+  // one with that sub-step's MFMAs.
+  auto compute = [&](auto p, const char* As, const char* Bs, auto nv_tag, auto&& stage_work) {
+    typedef decltype(nv_tag) NV;
+    typename MF::Frag fa[2][C::FM], fb[2][C::FN];
+    static_for<0, C::FM>([&](auto i) { fa[0][i] = frag_a(As, i, 0); });
+    static_for<0, C::FN>([&](auto j) { fb[0][j] = frag_b(Bs, j, 0); });
+    // LDS read instructions per sub-step (a bf16 MN-major fragment takes two)
+    constexpr int NR = C::FM * (C::AKC || C::ES == 4 ? 1 : 2) + C::FN * (C::BKC || C::ES == 4 ? 1 : 2);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // sub-step 0's reads lead
+    static_for<0, KK>([&](auto kk) {
+      constexpr int cur = kk & 1, nxt = cur ^ 1;
+      constexpr int nv = NV::at(kk);
+      if constexpr (kk + 1 < KK) {
+        const int k = (kk + 1) * MF::KI;
+        static_for<0, C::FM>([&](auto i) { fa[nxt][i] = frag_a(As, i, k); });
+        static_for<0, C::FN>([&](auto j) { fb[nxt][j] = frag_b(Bs, j, k); });
+      }
+      static_for<0, C::FM>([&](auto i) {
+        static_for<0, C::FN>([&](auto j) { acc[p][i][j] = MF::mma(fa[cur][i], fb[cur][j], acc[p][i][j]); });
       });
-    };
-
-    constexpr int L = DA::INSTR + DB::INSTR;  // loads per wave per K slab
-    // The compiler cannot tell the transposing LDS reads apart from the
-    // slab being loaded into another stage, and waits for every load in
-    // flight before each of them. With an MN-major operand the next slab is
-    // therefore issued in the last sub-step, after the stage's last reads.
-    typedef std::conditional_t<C::AKC && C::BKC, SlabPlan<DA::INSTR, 0, DB::INSTR, 1>,
-                               SlabPlan<DA::INSTR, KK - 1, DB::INSTR, KK - 1>> Plan;
-    constexpr int NS = C::NSTAGE;
-    // Every step issues exactly one slab (past the end of K, out of range),
-    // so L * (NS-2) loads still outstanding means slab kt has landed.
-    static_for<0, NS - 1>([&](auto s) {
-      const uint32_t oob = s() < KT ? 0u : 0x80000000u;
-      char* st = smem + s() * C::STAGE_BYTES;
-      DA::issue(ra, lda_b, kbeg + s() * C::BK, st, wave, lane, oob);
-      DB::issue(rb, ldb_b, kbeg + s() * C::BK, st + C::A_BYTES, wave, lane, oob);
+      if constexpr (nv > 0) stage_work(kk);
+      // Issue order: every fragment read of sub-step kk+1, then the MFMAs of
+      // sub-step kk (with the slab loads, if any, one after every few
+      // MFMAs), so the reads have a whole sub-step of MFMAs to land (left
+      // alone, the scheduler issues each read just before its use).
+      if constexpr (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+      if constexpr (nv > 0) {
+        constexpr int NM = C::FM * C::FN;
+        static_for<0, nv>([&](auto v) {
+          constexpr int m = (NM * (v + 1)) / nv - (NM * v) / nv;  // MFMAs after load v
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+        });
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
+      }
+      // The WN waves of a wave row hold the same A fragments; each takes
+      // every WN-th sub-step (a wave-uniform branch), so the sums cost each
+      // wave 1/WN of the dot products.
+      if constexpr (RSS) {
+        if (wn == kk % C::WN) static_for<0, C::FM>([&](auto i) { ss[i] = frag_sumsq(fa[cur][i], ss[i]); });
+      }
     });
-    int cur = 0;       // stage read in this step
-    int nxt = NS - 1;  // stage refilled in this step
+  };
+
+  constexpr int L = DA::INSTR + DB::INSTR;  // loads per wave per K slab
+  // The compiler cannot tell the transposing LDS reads apart from the
+  // slab being loaded into another stage, and waits for every load in
+  // flight before each of them. With an M/N-major operand the next slab is
+  // therefore issued in the last sub-step, after the stage's last reads.
+  typedef std::conditional_t<C::AKC && C::BKC, SlabPlan<DA::INSTR, 0, DB::INSTR, 1>,
+                             SlabPlan<DA::INSTR, KK - 1, DB::INSTR, KK - 1>> Plan;
+  constexpr int NS = C::NSTAGE;
+
+  // The slabs of all accumulators form one sequence (operand pair 0's KT
+  // slabs, then pair 1's, ...) streamed through one pipeline, so the loads
+  // of the next pair overlap the last steps of the current one. The cursor
+  // (iq, ik) names the next slab to issue; past the end of the sequence the
+  // loads are issued out of range and fetch nothing. Every step issues
+  // exactly one slab, so L * (NS-2) loads still outstanding means the slab
+  // to be read has landed.
+  int iq = 0, ik = 0;
+  auto issue_slab = [&](char* st, auto a_tag, auto b_tag) {
+    const bool live = iq < C::NACC && ik < KT;
+    const int q = live ? iq : 0;
+    const uint32_t oob = live ? 0u : 0x80000000u;
+    const int k0 = kbeg + ik * C::BK;
+    __amdgpu_buffer_rsrc_t rsa = ra[0], rsb = rb[0];
+    int64_t la = lda_b[0], lb = ldb_b[0];
+    static_for<1, C::NACC>([&](auto p) {
+      if (q == p) { rsa = ra[p]; rsb = rb[p]; la = lda_b[p]; lb = ldb_b[p]; }
+    });
+    if constexpr (decltype(a_tag)::value) DA::issue(rsa, la, k0, st, wave, lane, oob);
+    if constexpr (decltype(b_tag)::value) DB::issue(rsb, lb, k0, st + C::A_BYTES, wave, lane, oob);
+  };
+  auto advance = [&]() {
+    if (++ik >= KT) { ik = 0; ++iq; }
+  };
+  static_for<0, NS - 1>([&](auto s) {
+    issue_slab(smem + s() * C::STAGE_BYTES, std::true_type{}, std::true_type{});
+    advance();
+  });
+  int cur = 0;       // stage read in this step
+  int nxt = NS - 1;  // stage refilled in this step
+  static_for<0, C::NACC>([&](auto p) {
     for (int kt = 0; kt < KT; ++kt) {
-      // Slabs kt .. kt+NS-2 are in flight; wait for slab kt only.
+      // Slabs of the next NS-1 steps are in flight; wait for this one only.
       wait_vmcnt<L * (NS - 2)>();
       // A plain s_barrier: __syncthreads() would add a release fence that
       // waits for every outstanding load, including the slabs still allowed
@@ -648,25 +680,22 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      // Slab kt+NS-1 goes to the stage last read in step kt-1, which every
-      // wave has finished once past the barrier. Past the end of K the loads
-      // are issued out of range and fetch nothing.
-      const int ks = kt + NS - 1;
-      const uint32_t oob = ks < KT ? 0u : 0x80000000u;
+      // The slab NS-1 steps ahead goes to the stage last read in the
+      // previous step, which every wave has finished once past the barrier.
       char* st = smem + nxt * C::STAGE_BYTES;
       const char* As = smem + cur * C::STAGE_BYTES;
-      compute(As, As + C::A_BYTES, Plan{}, [&](auto kk) {
-        if constexpr (kk == Plan::A_AT) DA::issue(ra, lda_b, kbeg + ks * C::BK, st, wave, lane, oob);
-        if constexpr (kk == Plan::B_AT) DB::issue(rb, ldb_b, kbeg + ks * C::BK, st + C::A_BYTES, wave, lane, oob);
+      compute(p, As, As + C::A_BYTES, Plan{}, [&](auto kk) {
+        issue_slab(st, std::bool_constant<kk == Plan::A_AT>{}, std::bool_constant<kk == Plan::B_AT>{});
       });
+      advance();
       cur = cur + 1 == NS ? 0 : cur + 1;
       nxt = nxt + 1 == NS ? 0 : nxt + 1;
     }
-    // Out-of-range loads still count; none may land after the epilogue
-    // starts reusing this LDS (or the next accumulator's prologue refills it).
-    wait_vmcnt<0>();
-    __syncthreads();
   });
+  // Out-of-range loads still count; none may land after the epilogue
+  // starts reusing this LDS.
+  wait_vmcnt<0>();
+  __syncthreads();
 
   float* rowv = reinterpret_cast<float*>(smem + C::SCR_BYTES);
   float* colv = rowv + C::BM;
