@@ -74,24 +74,30 @@ def mlp_kernel_flops(T, d, r, ffn):
     }
 
 
-def mlp_kernel_bytes(T, d, r, ffn):
-    """Algorithmic HBM bytes per launch of the MLP step's kernels: each input
-    read once, each output written once (bf16 2 B, fp32 4 B)."""
+def mlp_kernel_rw(T, d, r, ffn):
+    """Algorithmic HBM bytes per launch of the MLP step's kernels as (read,
+    written): each input read once, each output written once (bf16 2 B,
+    fp32 4 B)."""
     b, f = 2, 4
     return {
-        "mlp_down1": T * d * b + d * 2 * r * b + T * 2 * r * (f + b) + T * f,
-        "mlp_up1_swiglu": T * 2 * r * b + 2 * r * ffn * b + T * ffn * b,
-        "mlp_down2": T * ffn * b + ffn * r * b + T * r * (f + b),
-        "mlp_up2": T * r * b + r * d * b + T * d * b,
-        "mlp_ds2": T * d * b + r * d * b + T * r * f + 2 * T * r * b,
-        "mlp_dB2": T * r * b + T * d * b + r * d * f,
-        "mlp_recompute_swiglu_bwd": T * 2 * r * b + 2 * r * ffn * b + T * r * b + ffn * r * b + 3 * T * ffn * b,
-        "mlp_dA2": T * ffn * b + T * r * b + ffn * r * f,
-        "mlp1_ds": 2 * T * ffn * b + 2 * r * ffn * b + T * 2 * r * f + T * 2 * r * b,
-        "mlp1_dB": T * 2 * r * b + 2 * T * ffn * b + 2 * r * ffn * f,
-        "mlp1_dA": T * d * b + T * 2 * r * b + d * 2 * r * f,
-        "mlp1_dx": T * 2 * r * b + d * 2 * r * b + 2 * T * d * b,
+        "mlp_down1": (T * d * b + d * 2 * r * b, T * 2 * r * (f + b) + T * f),
+        "mlp_up1_swiglu": (T * 2 * r * b + 2 * r * ffn * b, T * ffn * b),
+        "mlp_down2": (T * ffn * b + ffn * r * b, T * r * (f + b)),
+        "mlp_up2": (T * r * b + r * d * b, T * d * b),
+        "mlp_ds2": (T * d * b + r * d * b + T * r * f, 2 * T * r * b),
+        "mlp_dB2": (T * r * b + T * d * b, r * d * f),
+        "mlp_recompute_swiglu_bwd": (T * 2 * r * b + 2 * r * ffn * b + T * r * b + ffn * r * b, 3 * T * ffn * b),
+        "mlp_dA2": (T * ffn * b + T * r * b, ffn * r * f),
+        "mlp1_ds": (2 * T * ffn * b + 2 * r * ffn * b + T * 2 * r * f, T * 2 * r * b),
+        "mlp1_dB": (T * 2 * r * b + 2 * T * ffn * b, 2 * r * ffn * f),
+        "mlp1_dA": (T * d * b + T * 2 * r * b, d * 2 * r * f),
+        "mlp1_dx": (T * 2 * r * b + d * 2 * r * b + T * d * b, T * d * b),
     }
+
+
+def mlp_kernel_bytes(T, d, r, ffn):
+    """Algorithmic HBM bytes per launch (read + written)."""
+    return {k: rd + wr for k, (rd, wr) in mlp_kernel_rw(T, d, r, ffn).items()}
 
 
 def lrblock_kernel_flops(T, d, r, G, n, bwd=True):
@@ -459,11 +465,15 @@ MLP_LABEL_PATTERNS = {
 
 def short_kernel_name(n: str) -> str:
     import re
-    m = re.search(r"CfgI(DF16b|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELb(\d)ELb(\d)ELi(\d)EEENS_(\d+)(\w+?)(ILb(\d)EE)?EEE", n)
+    m = re.search(r"CfgI(DF16b|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELb(\d)ELb(\d)ELi(\d)EEENS_(\d+)", n)
     if m:
         t = "bf16" if m.group(1) == "DF16b" else "f32"
         lay = ("KC" if m.group(6) == "1" else "MC") + "/" + ("KC" if m.group(7) == "1" else "NC")
-        epi = m.group(10) + (f"<{m.group(12)}>" if m.group(12) else "")
+        rest = n[m.end():]
+        epi = rest[:int(m.group(9))]  # mangled <length><name>
+        flags = re.match(r"I((?:Lb\d+E)+)E", rest[len(epi):])
+        if flags:
+            epi += "<" + ",".join(re.findall(r"Lb(\d+)E", flags.group(1))) + ">"
         return f"gemm {t} {m.group(2)}x{m.group(3)} waves {m.group(4)}x{m.group(5)} {lay} nacc={m.group(8)} {epi}"
     return n.split("(")[0].replace("void ", "")
 
@@ -545,6 +555,33 @@ def traffic_json(fetch_csv: str, write_csv: str, workload: str, copy_mib: int) -
                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
             "kernels": kernels}
 
+def traffic_table(json_path: str, title: str, command: str) -> str:
+    """Markdown table of the per-launch traffic in a traffic JSON against the
+    algorithmic bytes of each launch."""
+    tj = json.load(open(json_path))
+    w = synth.WORKLOADS[tj["workload"]]
+    rw = mlp_kernel_rw(w["T"], w["d"], w["r"], w["ffn"])
+    cal = tj["calibration"]
+    out = [f"# {title}", "", "Commands (R = repository root):", "", "```", command, "```", "",
+           f"Calibration: each run first copies {cal['copy_bytes'] >> 20} MiB with one blit kernel. FETCH_SIZE read "
+           f"{cal['fetch_kib_read']:.0f} KiB for it (scale x{cal['fetch_scale']}), WRITE_SIZE "
+           f"{cal['write_kib_read']:.0f} KiB (scale x{cal['write_scale']}); both scales are applied below. "
+           "FETCH_SIZE counts every L2 miss that goes to the memory fabric, so reads served by the 256 MB "
+           "last-level (MALL) cache count too: fetched bytes are upper bounds on DRAM bytes.", "",
+           f"Source digest of the kernels measured: `{tj['source_digest']}`.", "",
+           "Algorithmic bytes: each input read once, each output written once (the operands of every launch are "
+           "listed in `mlp_kernel_rw` in bench.py). Fetched bytes above the algorithmic reads are operand panels "
+           "that many tiles share and that leave an XCD's 4 MB L2 between the waves of tiles using them (the "
+           "up projections and the recompute, with K = r, re-read their S1/B1 panels once per wave of tiles); "
+           "they are served from the fabric (MALL or DRAM).", "",
+           "| launch | kernel | fetched MB | written MB | algorithmic read MB | algorithmic write MB | "
+           "fetched / algorithmic read |", "|---|---|---|---|---|---|---|"]
+    for label, k in tj["kernels"].items():
+        rd, wr = rw[label]
+        out.append(f"| {label} | {k['kernel']} | {k['fetch_bytes'] / 1e6:.0f} | {k['write_bytes'] / 1e6:.0f} | "
+                   f"{rd / 1e6:.0f} | {wr / 1e6:.0f} | {k['fetch_bytes'] / rd:.2f} |")
+    return "\n".join(out) + "\n"
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -569,6 +606,8 @@ def main():
     ap.add_argument("--mfma-summary", metavar="CSV", help="print MFMA utilisation per kernel from a rocprofv3 "
                     "--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 counter_collection.csv (with --title, --command) "
                     "and exit")
+    ap.add_argument("--traffic-table", metavar="JSON", help="print a markdown table of a traffic JSON (written "
+                    "by --traffic) against the algorithmic bytes (with --title, --command) and exit")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
@@ -577,6 +616,9 @@ def main():
         return
     if args.mfma_summary:
         sys.stdout.write(mfma_summary(args.mfma_summary, args.title, args.command))
+        return
+    if args.traffic_table:
+        sys.stdout.write(traffic_table(args.traffic_table, args.title, args.command))
         return
     if args.traffic:
         print(json.dumps(traffic_json(args.traffic[0], args.traffic[1], args.workload,
