@@ -425,7 +425,13 @@ def cpu_baseline(name, target_s):
     dt, _ = run(probe)
     Ts = int(min(T, max(probe, probe * target_s / max(dt, 1e-3))))
     Ts = max(64, Ts // 64 * 64) if T >= 64 else T
+    # Where the whole workload takes less than the target, it is timed over
+    # several passes (each timed on its own; inputs drawn outside the timing).
     dt, fl = run(Ts)
+    passes = 1
+    while dt < 0.8 * target_s and passes < 8:
+        d2, f2 = run(Ts)
+        dt, fl, passes = dt + d2, fl + f2, passes + 1
     cpu_model, blas = "unknown", "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -441,8 +447,8 @@ def cpu_baseline(name, target_s):
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model, "blas": blas,
             "sample": f"fp64 NumPy oracle, fwd+bwd of the first {Ts} of {T} tokens of the same workload "
-                      f"(algorithmic flops scaled to the sample), {dt:.1f} s",
-            "tokens_per_s": Ts / dt}
+                      f"(algorithmic flops scaled to the sample), {passes} pass(es), {dt:.1f} s",
+            "tokens_per_s": Ts * passes / dt}
 
 
 

@@ -110,6 +110,40 @@ def test_lrmlp_parity(B, case):
     compare_lrmlp(out, inp, dtype, act)
 
 
+# Long K = T against few output tiles: the weight gradients are split along K
+# (a ragged last split), written as fp32 partials and summed in split order by
+# the reduction kernel, which also applies the gain to dA.
+SPLITK_CASES = [
+    ("lrblock", (3000, 256, 64, 2, 128, "bf16", "silu", True)),
+    ("lrblock", (8000, 128, 64, 1, 64, "f32", "identity", True)),
+    ("lrmlp", (2500, 128, 64, 192, "bf16", "silu")),
+]
+
+
+@pytest.mark.parametrize("case", SPLITK_CASES, ids=lambda c: c[0] + "x" + "x".join(map(str, c[1])))
+def test_split_k_weight_gradients(B, case):
+    kind, c = case
+    say(f"split-K {kind} {c} seed=0")
+    B.profiler_enable(None, 4096)
+    try:
+        if kind == "lrblock":
+            T, d, r, G, d_out, dtype, act, norm = c
+            inp = synth.lrblock_inputs(T, d, r, G, d_out, dtype=dtype, seed=0, norm=norm)
+            out = run_lrblock(B, inp, dtype, act, norm)
+        else:
+            T, d, r, ffn, dtype, act = c
+            inp = synth.lrmlp_inputs(T, d, r, ffn, dtype=dtype, seed=0)
+            out = run_lrmlp(B, inp, dtype, act)
+        rep = B.profiler_report()
+    finally:
+        B.profiler_disable()
+    assert "splitk_reduce" in rep, sorted(rep)
+    if kind == "lrblock":
+        compare_lrblock(out, inp, dtype, act, norm)
+    else:
+        compare_lrmlp(out, inp, dtype, act)
+
+
 def run_btp(B, sh, dtype):
     z, Bs, gs, As, dp = (dev(sh[k], dtype) for k in ("z", "B_s", "g_s", "A_s", "dp"))
     ds = dev_f32(sh["ds"])
