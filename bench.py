@@ -633,8 +633,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharded design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(collectives, sharding and rank code are not part of it). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
