@@ -51,26 +51,29 @@ struct ProfRec {
   const char* label;
   hipEvent_t start, stop;
 };
+// The timer itself is single-threaded (enabled, used and reported from one
+// host thread); with it off, launches from any thread touch only their own
+// thread-local slot.
 struct Profiler {
   bool on = false;
   std::string filter;
   std::vector<ProfRec> recs;
   size_t used = 0;
-  int pending = -1;
 } g_prof;
+thread_local int t_prof_pending = -1;
 
 void prof_begin(const char* label, hipStream_t s) {
-  g_prof.pending = -1;
+  t_prof_pending = -1;
   if (!g_prof.on || g_prof.used >= g_prof.recs.size()) return;
   if (!g_prof.filter.empty() && !strstr(label, g_prof.filter.c_str())) return;
   ProfRec& r = g_prof.recs[g_prof.used];
   r.label = label;
-  if (hipEventRecord(r.start, s) == hipSuccess) g_prof.pending = (int)g_prof.used;
+  if (hipEventRecord(r.start, s) == hipSuccess) t_prof_pending = (int)g_prof.used;
 }
 void prof_end(hipStream_t s) {
-  if (g_prof.pending < 0) return;
-  if (hipEventRecord(g_prof.recs[g_prof.pending].stop, s) == hipSuccess) ++g_prof.used;
-  g_prof.pending = -1;
+  if (t_prof_pending < 0) return;
+  if (hipEventRecord(g_prof.recs[t_prof_pending].stop, s) == hipSuccess) ++g_prof.used;
+  t_prof_pending = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1184,13 +1187,19 @@ int boost_profiler_enable(const char* name_filter, int max_records) {
   if (max_records <= 0 || max_records > (1 << 20))
     return fail(BOOST_ERR_INVALID_VALUE, "max_records = %d out of range", max_records);
   g_prof.filter = name_filter ? name_filter : "";
-  g_prof.recs.resize((size_t)max_records);
-  for (auto& r : g_prof.recs) {
-    r.label = "";
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
-      g_prof.recs.clear();
+  g_prof.recs.reserve((size_t)max_records);
+  for (int i = 0; i < max_records; ++i) {
+    ProfRec r{"", nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess) {
+      boost_profiler_disable();
       return fail(BOOST_ERR_LAUNCH, "hipEventCreate failed");
     }
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+      hipEventDestroy(r.start);
+      boost_profiler_disable();
+      return fail(BOOST_ERR_LAUNCH, "hipEventCreate failed");
+    }
+    g_prof.recs.push_back(r);
   }
   g_prof.used = 0;
   g_prof.on = true;
