@@ -669,8 +669,11 @@ def main():
     rep = B.profiler_report()
     B.profiler_disable()
     per_kernel = {k: v[1] for k, v in rep.items()}
-    main_kernels = {k: v for k, v in per_kernel.items() if k not in SIDE_STREAM_LABELS}
-    dom = max(main_kernels or per_kernel, key=(main_kernels or per_kernel).get)
+    # The roofline kernel: the longest launch on the caller's stream among
+    # those with algorithmic flops (not the transposes or reductions).
+    main_kernels = {k: v for k, v in per_kernel.items() if k not in SIDE_STREAM_LABELS and k in wl.kflops}
+    cands = main_kernels or {k: v for k, v in per_kernel.items() if k in wl.kflops} or per_kernel
+    dom = max(cands, key=cands.get)
     log("kernel times in one step (ms):", json.dumps({k: round(v, 4) for k, v in
                                                        sorted(per_kernel.items(), key=lambda kv: -kv[1])}))
 

@@ -220,3 +220,25 @@ def test_chained_entry_points_validate_their_extra_arguments(B):
     m = B.lrmlp_desc(128, 256, 64, 192, B.DT_BF16)
     margs = [f(1 << 20) for _ in range(6)] + [f(1 << 20), f(1 << 20)] + [f(1 << 20) for _ in range(4)] + [f(1 << 20)]
     assert L.boost_lrmlp_fwd_chained(ctypes.byref(m), *margs, f(1 << 20), 1, None) == E_WS
+
+
+def test_binding_checks_operands_against_the_descriptor():
+    """The binding rejects operands whose shape, dtype or layout differ from
+    what the descriptor implies (the C ABI takes plain pointers and cannot)."""
+    import torch
+
+    from rank_bottleneck_online_amd import binding
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    assert binding._arg(torch.zeros(8, dtype=torch.bfloat16), (8,), torch.bfloat16, x, "g") is not None
+    with pytest.raises(ValueError, match="shape"):
+        binding._arg(torch.zeros(9, dtype=torch.bfloat16), (8,), torch.bfloat16, x, "g")
+    with pytest.raises(TypeError, match="dtype"):
+        binding._arg(torch.zeros(8, dtype=torch.float32), (8,), torch.bfloat16, x, "g")
+    with pytest.raises(ValueError, match="contiguous"):
+        binding._arg(torch.zeros(8, 4, dtype=torch.bfloat16).t(), (4, 8), torch.bfloat16, x, "A")
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        binding._arg([0.0] * 8, (8,), torch.bfloat16, x, "g")
+    assert binding._opt(None, (8,), torch.bfloat16, x, "g") is None
+    with pytest.raises(ValueError, match="GPU"):
+        binding._anchor(x, "x")
+    assert binding._nbytes(torch.zeros(10, dtype=torch.float32)) == 40

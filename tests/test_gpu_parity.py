@@ -200,3 +200,24 @@ def test_scale_invariance_with_zero_eps(B):
     ref = oracle.lrblock_forward(inp["x"], inp["g"], inp["A_cat"], inp["B"], act="silu", eps=0.0)["Y"]
     for y in outs:
         check("Y", y, ref, "bf16")
+
+
+def test_binding_rejects_mismatched_operands(B):
+    """Operands that disagree with the descriptor are refused before any
+    launch: a wrong down-weight shape, a gain of another dtype, a saved
+    bottleneck of the wrong width, an output buffer of the wrong shape."""
+    T, d, r, G, n = 64, 128, 64, 3, 128
+    say("binding operand checks (no launch)")
+    inp = synth.lrblock_inputs(T, d, r, G, n, dtype="bf16", seed=0)
+    x, g, A, Bw, dY = (dev(inp[k], "bf16") for k in ("x", "g", "A_cat", "B", "dY"))
+    with pytest.raises(ValueError, match="A_cat"):
+        B.lrblock_fwd(x, g, A[:, :-64].contiguous(), Bw)
+    with pytest.raises(TypeError, match="g has dtype"):
+        B.lrblock_fwd(x, g.float(), A, Bw)
+    Y, H, sumsq = B.lrblock_fwd(x, g, A, Bw)
+    with pytest.raises(ValueError, match="H has shape"):
+        B.lrblock_bwd(x, g, A, Bw, H[:, :-64].contiguous(), sumsq, dY)
+    with pytest.raises(ValueError, match="dx"):
+        B.lrblock_bwd(x, g, A, Bw, H, sumsq, dY, out=(torch.empty(T + 1, d, dtype=x.dtype, device=x.device),
+                                                      None, None, None))
+    torch.cuda.synchronize()
