@@ -50,6 +50,102 @@ __global__ __launch_bounds__(256) void transpose_scale_kernel(const T* __restric
   }
 }
 
+// Several bf16 weight transposes in one launch: job j turns in[b][r][c]
+// (R x C per batch) into out[b][c][r] = round(scale[r] * in[b][r][c]) (no
+// rounding when scale is null: the values are copied). Each workgroup
+// transposes a 128 x 64 block of one job: every thread loads two pairs of
+// vertically adjacent 16-byte row segments (four loads in flight), packs
+// the two rows of each column into one 32-bit word (the two neighbouring
+// elements of an output row) and writes the words to an LDS tile indexed
+// [column][row pair]; each thread then reads four consecutive words (eight
+// output elements) and stores them as one 16-byte vector. The tile row
+// stride of 65 words keeps both the word writes and reads free of bank
+// conflicts. R and C are multiples of 64; rows of a block past R are
+// skipped.
+struct TransposeJob {
+  const bf16* in;
+  const bf16* scale;  // per input row, or null
+  bf16* out;
+  int R, C;
+  int tiles_r, tiles_c;  // blocks per batch: ceil(R / 128) x C / 64
+  int first;             // first block index of this job
+};
+constexpr int kMaxTransposeJobs = 4;
+struct TransposeJobs {
+  TransposeJob j[kMaxTransposeJobs];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposeJobs jobs) {
+  constexpr int TS = 65;  // words per tile row
+  __shared__ uint32_t tile[64 * TS];
+  // The job is picked field by field with compile-time indices (a runtime
+  // index into the argument array would copy it to scratch memory).
+  TransposeJob J = jobs.j[0];
+#pragma unroll
+  for (int q = 1; q < kMaxTransposeJobs; ++q)
+    if (q < jobs.n && (int)blockIdx.x >= jobs.j[q].first) J = jobs.j[q];
+  const int local = (int)blockIdx.x - J.first;
+  const int per_batch = J.tiles_r * J.tiles_c;
+  const int b = local / per_batch, rem = local - b * per_batch;
+  const int tr = (rem / J.tiles_c) * 128, tc = (rem % J.tiles_c) * 64;
+  const bf16* src = J.in + (int64_t)b * J.R * J.C;
+  bf16* dst = J.out + (int64_t)b * J.R * J.C;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+
+  // Load: item (pair p, column chunk c8) covers input rows 2p, 2p+1 and
+  // columns c8 .. c8+7 of the block; a wave's 64 lanes take 8 pairs x 8
+  // chunks, so each input row segment read is a full 128-byte line.
+  float v[2][2][8];
+  int pr[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int p = 8 * (wave + 4 * q) + (lane >> 3), c8 = (lane & 7) * 8;
+    pr[q] = p;
+    const int r0 = tr + 2 * p;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (r0 < J.R) {
+        Vec8<bf16>::load(src, (int64_t)(r0 + h) * J.C + tc + c8, v[q][h]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q][h][e] = 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int p = pr[q], c8 = (lane & 7) * 8, r0 = tr + 2 * p;
+    float sc0 = 1.f, sc1 = 1.f;
+    if (J.scale && r0 < J.R) {
+      sc0 = Elem<bf16>::load(J.scale, r0);
+      sc1 = Elem<bf16>::load(J.scale, r0 + 1);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bf16x2 w;
+      w[0] = static_cast<bf16>(sc0 * v[q][0][e]);
+      w[1] = static_cast<bf16>(sc1 * v[q][1][e]);
+      tile[(c8 + e) * TS + p] = __builtin_bit_cast(uint32_t, w);
+    }
+  }
+  __syncthreads();
+  // Store: vector (column oc, pair group p4) = output row tc + oc, output
+  // columns tr + 8 p4 .. +7; 16 lanes cover one 256-byte output row segment.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = t + 256 * q;
+    const int oc = i >> 4, p4 = i & 15;
+    const int col = tr + 8 * p4;
+    if (col < J.R) {
+      u32x4 o;
+      const uint32_t* w = tile + oc * TS + 4 * p4;
+      o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
+      *reinterpret_cast<u32x4*>(dst + (int64_t)(tc + oc) * J.R + col) = o;
+    }
+  }
+}
+
 // S = act(H) in the storage dtype (bottleneck activation recompute).
 template <typename T>
 __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict__ H, T* __restrict__ S,

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <initializer_list>
 #include <vector>
 
 #include "../../include/boost_lrblock.h"
@@ -197,17 +198,43 @@ int grid_for(int64_t n, int per_thread = 1) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(blocks, 4096));
 }
 
-// out[b][c][r] = scale[r] * in[b][r][c] (scale may be null).
-int launch_transpose(int dtype, const void* in, const void* scale, void* out, int64_t R, int64_t C, int64_t batch,
-                     hipStream_t s) {
-  const dim3 grid((unsigned)(C / 64), (unsigned)(R / 64), (unsigned)batch);
+// One weight transpose: out[b][c][r] = scale[r] * in[b][r][c] (scale may be
+// null), R x C per batch, R and C multiples of 64.
+struct TJob {
+  const void* in;
+  const void* scale;
+  void* out;
+  int64_t R, C, batch;
+};
+
+// Runs up to kMaxTransposeJobs transposes: bf16 ones in a single launch,
+// fp32 ones (small test shapes) one launch each.
+int launch_transposes(int dtype, std::initializer_list<TJob> list, hipStream_t s) {
+  if (list.size() > (size_t)kMaxTransposeJobs) return fail(BOOST_ERR_INVALID_VALUE, "too many transposes");
   prof_begin("weight_transpose", s);
-  if (dtype == BOOST_DT_BF16)
-    hipLaunchKernelGGL(transpose_scale_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(in),
-                       static_cast<const bf16*>(scale), static_cast<bf16*>(out), (int)R, (int)C);
-  else
-    hipLaunchKernelGGL(transpose_scale_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(in),
-                       static_cast<const float*>(scale), static_cast<float*>(out), (int)R, (int)C);
+  if (dtype == BOOST_DT_BF16) {
+    TransposeJobs jobs{};
+    int64_t blocks = 0;
+    for (const TJob& t : list) {
+      TransposeJob& J = jobs.j[jobs.n++];
+      J.in = static_cast<const bf16*>(t.in);
+      J.scale = static_cast<const bf16*>(t.scale);
+      J.out = static_cast<bf16*>(t.out);
+      J.R = (int)t.R;
+      J.C = (int)t.C;
+      J.tiles_r = (int)cdiv((int)t.R, 128);
+      J.tiles_c = (int)(t.C / 64);
+      J.first = (int)blocks;
+      blocks += (int64_t)J.tiles_r * J.tiles_c * t.batch;
+    }
+    if (blocks > 0) hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, jobs);
+  } else {
+    for (const TJob& t : list) {
+      const dim3 grid((unsigned)(t.C / 64), (unsigned)(t.R / 64), (unsigned)t.batch);
+      hipLaunchKernelGGL(transpose_scale_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(t.in),
+                         static_cast<const float*>(t.scale), static_cast<float*>(t.out), (int)t.R, (int)t.C);
+    }
+  }
   prof_end(s);
   return check_launch("weight_transpose");
 }
@@ -465,8 +492,7 @@ int lrblock_fwd_impl(const boost_lrblock_desc* d, const void* x, const void* g, 
   void* AT = at(ws, p.f_AT);
   void* BT = at(ws, p.f_BT);
   // K-contiguous weight operands: (g * A_cat)^T [G*r, d] and B_j^T [d_out, r].
-  RBO_TRY(launch_transpose(dt, A_cat, d->norm ? g : nullptr, AT, D, G * r, 1, s));
-  RBO_TRY(launch_transpose(dt, B, nullptr, BT, r, n, G, s));
+  RBO_TRY(launch_transposes(dt, {{A_cat, d->norm ? g : nullptr, AT, D, G * r, 1}, {B, nullptr, BT, r, n, G}}, s));
   // Down: H = rho * (x @ (g * A_cat)), S = act(H), sumsq.
   {
     GemmOps ops{};
@@ -854,10 +880,12 @@ int boost_lrmlp_fwd_chained(const boost_lrmlp_desc* d, const void* x, const void
   void* S2 = at(ws, p.f_S2);
   const float inv = 1.f / (float)D;
   // K-contiguous weight operands (gain folded into the first down weights).
-  RBO_TRY(launch_transpose(dt, A1_cat, g, A1T, D, 2 * r, 1, s));
-  RBO_TRY(launch_transpose(dt, B1, nullptr, B1T, r, F, 2, s));
-  RBO_TRY(launch_transpose(dt, A2, nullptr, A2T, F, r, 1, s));
-  RBO_TRY(launch_transpose(dt, B2, nullptr, B2T, r, D, 1, s));
+  RBO_TRY(launch_transposes(dt,
+                            {{A1_cat, g, A1T, D, 2 * r, 1},
+                             {B1, nullptr, B1T, r, F, 2},
+                             {A2, nullptr, A2T, F, r, 1},
+                             {B2, nullptr, B2T, r, D, 1}},
+                            s));
   {  // H1 = rho * (x @ (g * A1_cat)), S1 = act(H1), sumsq
     GemmOps ops{};
     ops.a[0] = opnd(x, D, T, D, es);
@@ -973,7 +1001,7 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void
   // S1 = act(H1) recomputed from the saved bottleneck.
   RBO_TRY(launch_act_quant(dt, H1, S1, T * 2 * r, d->act, s));
   void* B1T = at(ws, p.b_B1T);
-  RBO_TRY(launch_transpose(dt, B1, nullptr, B1T, r, F, 2, s));
+  RBO_TRY(launch_transposes(dt, {{B1, nullptr, B1T, r, F, 2}}, s));
   {  // recompute Yg, Yu and dM = dU2 @ A2^T in the same tile; M, dYg, dYu
     GemmOps ops{};
     ops.a[0] = opnd(S1, 2 * r, T, r, es);
@@ -1041,8 +1069,7 @@ int boost_btp_share_fwd(const boost_btp_share_desc* d, const void* z, const void
   void* AT = at(ws, p.f_AT);
   void* ag = at(ws, p.f_ag);
   float* sp = reinterpret_cast<float*>(at(ws, p.f_sp));
-  RBO_TRY(launch_transpose(dt, B_s, nullptr, BT, r, S, 1, st));
-  RBO_TRY(launch_transpose(dt, A_s, nullptr, AT, S, r, 1, st));
+  RBO_TRY(launch_transposes(dt, {{B_s, nullptr, BT, r, S, 1}, {A_s, nullptr, AT, S, r, 1}}, st));
   {  // u = z @ B_s; a = SiLU(u); ag = a * g_s; row partials of a^2
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);
@@ -1098,7 +1125,7 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
     RBO_TRY((gemm<EpiStore<true>, true, true, 1>("btp_e", dt, p.e, T, S, r, 1, ops, ea, st)));
   }
   void* BT = at(ws, p.b_BT);
-  RBO_TRY(launch_transpose(dt, B_s, nullptr, BT, r, S, 1, st));
+  RBO_TRY(launch_transposes(dt, {{B_s, nullptr, BT, r, S, 1}}, st));
   {  // recompute u = z @ B_s; du, ag, dg partials
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);

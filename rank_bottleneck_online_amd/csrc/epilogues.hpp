@@ -12,7 +12,16 @@
 
 namespace rbo {
 
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + expf(-z)); }
+// sigmoid(z) = 1 / (1 + e^-z) = 1 / (1 + 2^(-z log2 e)), on the hardware
+// base-2 exponential and reciprocal (v_exp_f32, v_rcp_f32; about 1 ulp each,
+// far below the bf16 rounding every activation output goes through). The
+// libm-accurate exp and the IEEE division cost about 25 instructions per
+// element, which the epilogue of every tile pays with the matrix cores idle.
+// Limits: z -> -inf gives 2^+inf = inf and rcp(inf) = 0; z -> +inf gives 1.
+__device__ __forceinline__ float sigmoid_f(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return __builtin_amdgcn_rcpf(1.f + e);
+}
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 // d/dz SiLU(z) = s (1 + z (1 - s)), s = sigmoid(z)
 __device__ __forceinline__ float silu_grad_f(float z) {
