@@ -117,16 +117,19 @@ def recompute_flops(kind, w) -> float:
     if kind == "btp":
         return float(2 * w["T"] * w["r"] * (w["d_global"] // w["P"]))
     return 0.0
-# Launches the library puts on its side stream (weight gradients): they run
-# concurrently with the input-gradient chain, so their event durations
-# include sharing the GPU and they are not roofline candidates.
+# Weight-gradient launches: the library runs them on its side stream
+# concurrently with the input-gradient chain (the tensor-parallel share's
+# dB_s runs on the caller's stream, concurrently with dA_s on the side
+# stream), so their event durations include sharing the GPU and they are not
+# roofline candidates.
 SIDE_STREAM_LABELS = ("mlp_dB2", "mlp_dA2", "mlp1_dB", "mlp1_dA", "lrblock_dB", "lrblock_dA", "btp_dA", "btp_dB",
                       "splitk_reduce")
 
 
 def btp_kernel_flops(T, r, ds):
-    return {"btp_u": 2 * T * r * ds, "btp_p": 2 * T * ds * r, "btp_e": 2 * T * r * ds,
-            "btp_u_bwd": 2 * T * r * ds, "btp_dA": 2 * ds * r * T, "btp_dB": 2 * r * ds * T,
+    # btp_u_bwd: the recompute u = z @ B_s and e = dp @ A_s^T in one tile.
+    return {"btp_u": 2 * T * r * ds, "btp_p": 2 * T * ds * r,
+            "btp_u_bwd": 2 * 2 * T * r * ds, "btp_dA": 2 * ds * r * T, "btp_dB": 2 * r * ds * T,
             "btp_dz": 2 * T * ds * r}
 
 

@@ -681,9 +681,11 @@ int btp_check_desc(const boost_btp_share_desc* d) {
 }
 
 struct BtpPlan {
-  Choice u, p, e, dA, dB, dz;
+  Choice u, p, ue, dA, dB, dz;
   size_t f_BT, f_AT, f_ag, f_sp, fwd_bytes;
-  size_t b_BT, b_e, b_du, b_ag, b_dg, b_part, bwd_bytes;
+  // dA_s and dB_s run on different streams, so their split-K partials get
+  // separate buffers.
+  size_t b_BT, b_du, b_ag, b_dg, b_part_dA, b_part_dB, bwd_bytes;
 };
 
 BtpPlan btp_plan(const boost_btp_share_desc* d) {
@@ -692,7 +694,7 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   const int64_t T = d->T, r = d->r, S = d->d_shard, es = esize(dt);
   p.u = choose(dt, T, S, r, 1, false, false);
   p.p = choose(dt, T, r, S, 1, false, false);
-  p.e = choose(dt, T, S, r, 1, false, false);
+  p.ue = choose(dt, T, S, r, 1, false, true);
   p.dA = choose(dt, S, r, T, 1, true, false);
   p.dB = choose(dt, r, S, T, 1, true, false);
   p.dz = choose(dt, T, r, S, 1, false, false);
@@ -704,14 +706,11 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   p.fwd_bytes = f.total;
   WsLayout b;
   p.b_BT = b.take((size_t)(r * S * es));
-  p.b_e = b.take((size_t)(T * S * 4));
   p.b_du = b.take((size_t)(T * S * es));
   p.b_ag = b.take((size_t)(T * S * es));
-  p.b_dg = b.take((size_t)(p.u.tiles_m * S * 4));
-  size_t part = 0;
-  if (p.dA.splits > 1) part = std::max(part, (size_t)(p.dA.splits * S * r * 4));
-  if (p.dB.splits > 1) part = std::max(part, (size_t)(p.dB.splits * r * S * 4));
-  p.b_part = part ? b.take(part) : 0;
+  p.b_dg = b.take((size_t)(p.ue.tiles_m * S * 4));
+  p.b_part_dA = p.dA.splits > 1 ? b.take((size_t)(p.dA.splits * S * r * 4)) : 0;
+  p.b_part_dB = p.dB.splits > 1 ? b.take((size_t)(p.dB.splits * r * S * 4)) : 0;
   p.bwd_bytes = b.total;
   return p;
 }
@@ -1112,29 +1111,25 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
   RBO_TRY(check_ranges(rs));
   RBO_TRY(check_ws(ws, ws_bytes, p.bwd_bytes));
   hipStream_t st = as_stream(stream);
-  float* e = reinterpret_cast<float*>(at(ws, p.b_e));
   void* du = at(ws, p.b_du);
   void* ag = at(ws, p.b_ag);
   float* dgp = reinterpret_cast<float*>(at(ws, p.b_dg));
-  float* part = p.b_part ? reinterpret_cast<float*>(at(ws, p.b_part)) : nullptr;
-  {  // e = dp @ A_s^T (fp32)
-    GemmOps ops{};
-    ops.a[0] = opnd(dp, r, T, r, es);
-    ops.b[0] = opnd(A_s, r, S, r, es);
-    EpiStore<true>::Args ea{e, S, 0, nullptr};
-    RBO_TRY((gemm<EpiStore<true>, true, true, 1>("btp_e", dt, p.e, T, S, r, 1, ops, ea, st)));
-  }
+  float* part_dA = p.b_part_dA ? reinterpret_cast<float*>(at(ws, p.b_part_dA)) : nullptr;
+  float* part_dB = p.b_part_dB ? reinterpret_cast<float*>(at(ws, p.b_part_dB)) : nullptr;
   void* BT = at(ws, p.b_BT);
   RBO_TRY(launch_transposes(dt, {{B_s, nullptr, BT, r, S, 1}}, st));
-  {  // recompute u = z @ B_s; du, ag, dg partials
+  {  // recompute u = z @ B_s and e = dp @ A_s^T in the same tile; du, ag, dg partials
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);
     ops.b[0] = opnd(BT, r, S, r, es);
-    EpiBtpUBwd::Args ea{e, ds, g_s, du, ag, dgp, S};
-    RBO_TRY((gemm<EpiBtpUBwd, true, true, 1>("btp_u_bwd", dt, p.u, T, S, r, 1, ops, ea, st)));
+    ops.a[1] = opnd(dp, r, T, r, es);
+    ops.b[1] = opnd(A_s, r, S, r, es);
+    EpiBtpUBwd::Args ea{ds, g_s, du, ag, dgp, S};
+    RBO_TRY((gemm<EpiBtpUBwd, true, true, 2>("btp_u_bwd", dt, p.ue, T, S, r, 1, ops, ea, st)));
   }
-  RBO_TRY(launch_colsum(dgp, p.u.tiles_m, S, S, dg_s, st));
-  // Weight gradients on the side stream; dz on the caller's.
+  RBO_TRY(launch_colsum(dgp, p.ue.tiles_m, S, S, dg_s, st));
+  // dA_s on the side stream; dz, then dB_s, on the caller's (two weight
+  // gradients in a row on the side stream would finish well after dz).
   Side* side = nullptr;
   RBO_TRY(side_for_device(&side));
   RBO_TRY(stream_after(side->s, st, side));
@@ -1142,13 +1137,7 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
     GemmOps ops{};
     ops.a[0] = opnd(ag, S, T, S, es);
     ops.b[0] = opnd(dp, r, T, r, es);
-    RBO_TRY(wgrad("btp_dA", dt, p.dA, S, r, T, 1, ops, nullptr, dA_s, part, side->s));
-  }
-  {  // dB_s = z^T @ du
-    GemmOps ops{};
-    ops.a[0] = opnd(z, r, T, r, es);
-    ops.b[0] = opnd(du, S, T, S, es);
-    RBO_TRY(wgrad("btp_dB", dt, p.dB, r, S, T, 1, ops, nullptr, dB_s, part, side->s));
+    RBO_TRY(wgrad("btp_dA", dt, p.dA, S, r, T, 1, ops, nullptr, dA_s, part_dA, side->s));
   }
   {  // dz = du @ B_s^T
     GemmOps ops{};
@@ -1156,6 +1145,12 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
     ops.b[0] = opnd(B_s, S, r, S, es);
     EpiStore<false>::Args ea{dz, r, 0, nullptr};
     RBO_TRY((gemm<EpiStore<false>, true, true, 1>("btp_dz", dt, p.dz, T, r, S, 1, ops, ea, st)));
+  }
+  {  // dB_s = z^T @ du
+    GemmOps ops{};
+    ops.a[0] = opnd(z, r, T, r, es);
+    ops.b[0] = opnd(du, S, T, S, es);
+    RBO_TRY(wgrad("btp_dB", dt, p.dB, r, S, T, 1, ops, nullptr, dB_s, part_dB, st));
   }
   RBO_TRY(stream_after(st, side->s, side));
   return BOOST_OK;

@@ -509,19 +509,20 @@ struct EpiBtpP : EpiBase {
 };
 
 // ---------------------------------------------------------------------------
-// Tensor-parallel share, backward, recompute of u = z @ B_s (acc) fused with
-// the backward of SiLU, the gain and the local statistic:
-//   a = SiLU(u); da = g_s e + 2 ds a; du = da SiLU'(u)   (e = dp @ A_s^T, fp32)
+// Tensor-parallel share, backward: two accumulators over the same [T, d_s]
+// tile, the recompute u = z @ B_s and e = dp @ A_s^T (both K = r; e never
+// leaves the fp32 registers), fused with the backward of SiLU, the gain and
+// the local statistic:
+//   a = SiLU(u); da = g_s e + 2 ds a; du = da SiLU'(u)
 // writes du (dtype), a * g_s (dtype, operand of dA_s) and per-column
 // partials of dg_s = sum_t a e over this tile's rows.
 // ---------------------------------------------------------------------------
 struct EpiBtpUBwd : EpiBase {
   static constexpr bool kColSum = true;
   struct Pre {
-    float e[8], g[8];
+    float g[8];
   };
   struct Args {
-    const float* e;
     const float* ds;
     const void* g;
     void* du;
@@ -538,29 +539,28 @@ struct EpiBtpUBwd : EpiBase {
     typedef typename C::T T;
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
-    Vec8<float>::load(a.e, (int64_t)row * a.ld + col, pf.e);
     Vec8<T>::load(a.g, col, pf.g);
   }
   template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
                                                const float (&v)[C::NACC][8], const Pre& pf, float&, float (&colc)[8]) {
     typedef typename C::T T;
+    static_assert(C::NACC == 2, "the share's backward takes the u and e accumulators");
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
     const int64_t o = (int64_t)row * a.ld + col;
     const float dsv = c.rowv[lr];
     float du[8], ag[8];
-    const float (&ev)[8] = pf.e;
     const float (&gv)[8] = pf.g;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float u = v[0][e];
+      const float u = v[0][e], ev = v[1][e];
       const float s = sigmoid_f(u);
       const float av = u * s;
-      const float da = gv[e] * ev[e] + 2.f * dsv * av;
+      const float da = gv[e] * ev + 2.f * dsv * av;
       du[e] = da * (s * (1.f + u * (1.f - s)));
       ag[e] = av * gv[e];
-      colc[e] += av * ev[e];
+      colc[e] += av * ev;
     }
     Vec8<T>::store(a.du, o, du);
     Vec8<T>::store(a.ag, o, ag);
