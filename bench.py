@@ -591,6 +591,33 @@ def traffic_table(json_path: str, title: str, command: str) -> str:
                    f"{rd / 1e6:.0f} | {wr / 1e6:.0f} | {k['fetch_bytes'] / rd:.2f} |")
     return "\n".join(out) + "\n"
 
+def r_sweep(B, torch, ranks, steps, warmup):
+    """Per-launch kernel times of the 7B-shaped MLP block at several ranks."""
+    w = synth.WORKLOADS["llama2_7b_mlp"]
+    T, d, ffn = w["T"], w["d"], w["ffn"]
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    for r in ranks:
+        def rn(*shape, std=1.0):
+            return (torch.randn(*shape, device="cuda", generator=gen) * std).bfloat16()
+        x, dY = rn(T, d), rn(T, d)
+        g = (1 + 0.1 * torch.randn(d, device="cuda", generator=gen)).bfloat16()
+        args = [x, g, rn(d, 2 * r, std=d ** -0.5), rn(2, r, ffn, std=r ** -0.5), rn(ffn, r, std=ffn ** -0.5),
+                rn(r, d, std=r ** -0.5)]
+        for _ in range(max(1, warmup)):
+            fo = B.lrmlp_fwd(*args)
+            B.lrmlp_bwd(*args, *fo[1:], dY)
+        torch.cuda.synchronize()
+        B.profiler_enable(None, 4096)
+        for _ in range(max(1, steps)):
+            fo = B.lrmlp_fwd(*args)
+            B.lrmlp_bwd(*args, *fo[1:], dY)
+        torch.cuda.synchronize()
+        rep = B.profiler_report()
+        B.profiler_disable()
+        print(json.dumps({"T": T, "d": d, "r": r, "ffn": ffn,
+                          "kernel_ms": {k: round(v[1] / v[0], 4) for k, v in sorted(rep.items())}}), flush=True)
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -617,6 +644,11 @@ def main():
                     "and exit")
     ap.add_argument("--traffic-table", metavar="JSON", help="print a markdown table of a traffic JSON (written "
                     "by --traffic) against the algorithmic bytes (with --title, --command) and exit")
+    ap.add_argument("--r-sweep", metavar="R,R,...", help="time the 7B-shaped MLP block (T, d, ffn of the default "
+                    "workload) at each listed rank r with seeded Gaussian inputs generated on the GPU, print one JSON "
+                    "line of per-launch kernel times (ms, library events, mean of --steps steps) per rank, and exit. "
+                    "The K = r products have a fixed tile count, so their time against r separates the fixed "
+                    "per-tile cost from the main loop")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
@@ -646,6 +678,10 @@ def main():
         sys.exit(1)
     from rank_bottleneck_online_amd import binding as B
     B.lib()
+
+    if args.r_sweep:
+        r_sweep(B, torch, [int(v) for v in args.r_sweep.split(",")], args.steps, args.warmup)
+        return
 
     wl = Workload(args.workload)
     if args.act and wl.kind == "layerset":
