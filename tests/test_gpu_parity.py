@@ -100,7 +100,9 @@ def compare_lrmlp(out, inp, dtype, act, eps=1e-5, report=None):
 
 
 @pytest.mark.parametrize("case", [(300, 256, 128, 448, "bf16", "silu"), (300, 256, 128, 448, "bf16", "identity"),
-                                  (96, 128, 64, 192, "f32", "silu"), (513, 512, 128, 1408, "bf16", "silu")],
+                                  (96, 128, 64, 192, "f32", "silu"), (513, 512, 128, 1408, "bf16", "silu"),
+                                  (1, 128, 64, 192, "bf16", "silu"),       # a single token
+                                  (70, 64, 64, 64, "f32", "identity")],    # the smallest widths, ragged T
                          ids=lambda c: "x".join(map(str, c)))
 def test_lrmlp_parity(B, case):
     T, d, r, ffn, dtype, act = case
