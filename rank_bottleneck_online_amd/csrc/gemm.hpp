@@ -447,7 +447,12 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
           });
         });
       });
-      __syncthreads();
+      // Each wave stages into and reads back from its own LDS region, and
+      // a wave's LDS accesses complete in order, so no workgroup barrier is
+      // needed around a staging round (a barrier's release fence would also
+      // wait for the output stores already issued); the empty asm keeps the
+      // compiler from moving the accesses across each other.
+      asm volatile("" ::: "memory");
       static_for<0, STEPS>([&](auto s) {
         const int r = s * RPS + rsub;
         const int lr = c.wm * C::WTM + i * 32 + h * ER + r;
@@ -469,7 +474,7 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
           if (c8 == 0) c.rowpart[c.wn * C::BM + lr] = rowc;
         }
       });
-      __syncthreads();
+      asm volatile("" ::: "memory");
     });
   });
 
