@@ -1,0 +1,100 @@
+"""CPU tests of the benchmark's host-side accounting and profile tooling.
+
+No GPU: the algorithmic flop counts of the workloads against the step's
+structure (three times the forward products plus the prescribed recompute),
+the kernel-name shortener used by the profile summaries, the calibration of
+the FETCH_SIZE / WRITE_SIZE counters, and the one-GPU guard.
+"""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from rank_bottleneck_online_amd import synth  # noqa: E402
+
+SWIGLU_BWD = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi256ELi128ELi4ELi2ELb1ELb1ELi3EEENS_12EpiSwigluBwdEEEvNS_8"
+              "GemmGeomENS_7GemmOpsENT0_4ArgsE")
+DOWN1 = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi256ELi256ELi2ELi4ELb1ELb1ELi1EEENS_7EpiDownILb1ELb0EEEEEvNS_8"
+         "GemmGeomENS_7GemmOpsENT0_4ArgsE")
+WGRAD = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi128ELi128ELi2ELi4ELb0ELb0ELi1EEENS_8EpiStoreILb1EEEEEvNS_8"
+         "GemmGeomENS_7GemmOpsENT0_4ArgsE")
+
+
+def test_mlp_step_flops_are_three_forwards_plus_the_recompute():
+    w = synth.WORKLOADS["llama2_7b_mlp"]
+    k = bench.mlp_kernel_flops(w["T"], w["d"], w["r"], w["ffn"])
+    fwd = sum(k[n] for n in ("mlp_down1", "mlp_up1_swiglu", "mlp_down2", "mlp_up2"))
+    rec = bench.recompute_flops("lrmlp", w)
+    assert sum(k.values()) == 3 * fwd + rec
+    assert round(sum(k.values()) / 1e9, 1) == 2650.0
+
+
+def test_btp_share_flops_are_three_forwards_plus_the_recompute():
+    w = synth.WORKLOADS["llama2_13b_btp_share_tp4"]
+    ds = w["d_global"] // w["P"]
+    k = bench.btp_kernel_flops(w["T"], w["r"], ds)
+    fwd = k["btp_u"] + k["btp_p"]
+    assert sum(k.values()) == 3 * fwd + bench.recompute_flops("btp", w)
+    # the u recompute and e = dp A_s^T share one launch
+    assert k["btp_u_bwd"] == 2 * k["btp_u"]
+
+
+def test_lrblock_backward_is_twice_the_forward():
+    k = bench.lrblock_kernel_flops(300, 512, 128, 3, 320, bwd=True)
+    fwd = k["lrblock_down"] + k["lrblock_up"]
+    assert sum(k.values()) == 3 * fwd
+
+
+def test_short_kernel_names():
+    assert bench.short_kernel_name(SWIGLU_BWD) == "gemm bf16 256x128 waves 4x2 KC/KC nacc=3 EpiSwigluBwd"
+    assert bench.short_kernel_name(DOWN1) == "gemm bf16 256x256 waves 2x4 KC/KC nacc=1 EpiDown<1,0>"
+    assert bench.short_kernel_name(WGRAD) == "gemm bf16 128x128 waves 2x4 MC/NC nacc=1 EpiStore<1>"
+    assert bench.short_kernel_name("void rbo::colsum_kernel(float const*)") == "rbo::colsum_kernel"
+
+
+def _counter_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for name, counter, value in rows:
+            wr.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_traffic_calibration(tmp_path):
+    # A 1 GiB copy that FETCH_SIZE reports as half its size and WRITE_SIZE
+    # as its size: fetched bytes are scaled by 2, written bytes by 1; two
+    # dispatches of a kernel are averaged.
+    fetch, write = str(tmp_path / "f.csv"), str(tmp_path / "w.csv")
+    _counter_csv(fetch, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288.0),
+                         (SWIGLU_BWD, "FETCH_SIZE", 1000.0), (SWIGLU_BWD, "FETCH_SIZE", 3000.0)])
+    _counter_csv(write, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0),
+                         (SWIGLU_BWD, "WRITE_SIZE", 500.0), (SWIGLU_BWD, "WRITE_SIZE", 500.0)])
+    tj = bench.traffic_json(fetch, write, "llama2_7b_mlp", 1024)
+    assert tj["calibration"]["fetch_scale"] == pytest.approx(2.0)
+    assert tj["calibration"]["write_scale"] == pytest.approx(1.0)
+    k = tj["kernels"]["mlp_recompute_swiglu_bwd"]
+    assert k["dispatches"] == 2
+    assert k["fetch_bytes"] == 2000 * 1024 * 2
+    assert k["write_bytes"] == 500 * 1024
+    assert tj["source_digest"] == bench.source_digest()
+
+
+def test_traffic_needs_the_calibration_copy(tmp_path):
+    fetch, write = str(tmp_path / "f.csv"), str(tmp_path / "w.csv")
+    _counter_csv(fetch, [(SWIGLU_BWD, "FETCH_SIZE", 1000.0)])
+    _counter_csv(write, [(SWIGLU_BWD, "WRITE_SIZE", 500.0)])
+    with pytest.raises(SystemExit):
+        bench.traffic_json(fetch, write, "llama2_7b_mlp", 1024)
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
