@@ -629,6 +629,9 @@ def main():
     ap.add_argument("--act", default=None, help="bottleneck activation for the layer set (silu|identity)")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--graph-steps", type=int, default=0,
+                    help="after the timed steps, capture one forward+backward step into a HIP graph and time this "
+                         "many replays (reported under timing.graph; `value` stays the eager rate)")
     ap.add_argument("--flush-steps", type=int, default=5,
                     help="steps of a second, untimed-for-value pass with the last-level cache flushed before each")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -758,6 +761,29 @@ def main():
                    "tflops_median": round(wl.flops / (fms[len(fms) // 2] * 1e-3) / 1e12, 2)}
         del scratch
 
+    # Optional: the same step captured into a HIP graph and replayed (the
+    # library allocates nothing and forks its side stream with events, which
+    # capture records as graph dependencies); launch-bound workloads show the
+    # launch overhead this removes.
+    graph = None
+    if args.graph_steps > 0:
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            wl.step()
+        torch.cuda.synchronize()
+        gl = []
+        for _ in range(args.graph_steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            cg.replay()
+            b.record(stream)
+            gl.append((a, b))
+        torch.cuda.synchronize()
+        gms = sorted(a.elapsed_time(b) for a, b in gl)
+        graph = {"steps": args.graph_steps, "ms_median": round(gms[len(gms) // 2], 4), "ms_min": round(gms[0], 4),
+                 "tflops_median": round(wl.flops / (gms[len(gms) // 2] * 1e-3) / 1e12, 3)}
+        del cg
+
     cnt, tot = rep.get(dom, (0, 0.0))
     avg_ms = tot / max(cnt, 1)
     launches_per_step = cnt / args.steps
@@ -831,7 +857,7 @@ def main():
                    "bwd_ms_min": round(min(bwd_ms), 4) if wl.bwd_fn else None,
                    "model_only_tflops": round(wl.model_flops / (ms * 1e-3) / 1e12, 2),
                    "model_only_gflop_per_step": round(wl.model_flops / 1e9, 2),
-                   "mall_flushed": flushed},
+                   "mall_flushed": flushed, "graph": graph},
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
