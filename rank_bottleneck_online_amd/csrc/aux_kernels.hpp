@@ -174,15 +174,24 @@ __global__ __launch_bounds__(256) void act_quant_bf16x8_kernel(const float4* __r
   }
 }
 
-// out[n] = sum_{p < P} part[p * stride + n], in order p = 0, 1, ...
+// out[n] = sum_{p < P} part[p * stride + n] in a fixed order: each of four
+// threads of a column sums a contiguous quarter of the partials in order,
+// and the four quarter sums are added in order 0, 1, 2, 3. A workgroup
+// covers 64 columns, so the grid spans N / 64 workgroups and each thread
+// has about P / 4 independent loads in flight.
+constexpr int kColsumCols = 64;
 __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ part, int P, int64_t stride,
                                                      int64_t N, float* __restrict__ out) {
-  for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < N;
-       n += (int64_t)gridDim.x * blockDim.x) {
-    float s = 0.f;
-    for (int p = 0; p < P; ++p) s += part[(int64_t)p * stride + n];
-    out[n] = s;
-  }
+  __shared__ float q[4][kColsumCols];
+  const int c = threadIdx.x & (kColsumCols - 1), h = threadIdx.x / kColsumCols;
+  const int64_t n = (int64_t)blockIdx.x * kColsumCols + c;
+  const int p0 = (h * P) / 4, p1 = ((h + 1) * P) / 4;
+  float s = 0.f;
+  if (n < N)
+    for (int p = p0; p < p1; ++p) s += part[(int64_t)p * stride + n];
+  q[h][c] = s;
+  __syncthreads();
+  if (h == 0 && n < N) out[n] = ((q[0][c] + q[1][c]) + q[2][c]) + q[3][c];
 }
 
 // Split-K reduction: part is [batch][S][MN]; out[b][e] = rowscale[e / cols] *
