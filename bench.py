@@ -469,6 +469,11 @@ MLP_LABEL_PATTERNS = {
     "mlp1_dx": "NS_5EpiDXE",
     "mlp1_ds": "NS_5EpiDSILb1",
     "mlp_ds2": "NS_5EpiDSILb0",
+    # weight-gradient products: one kernel instantiation per launch tag
+    "mlp1_dB": "NS_8EpiStoreILb1EEELi1EE",
+    "mlp1_dA": "NS_8EpiStoreILb1EEELi2EE",
+    "mlp_dB2": "NS_8EpiStoreILb1EEELi3EE",
+    "mlp_dA2": "NS_8EpiStoreILb1EEELi4EE",
 }
 
 
@@ -483,7 +488,9 @@ def short_kernel_name(n: str) -> str:
         flags = re.match(r"I((?:Lb\d+E)+)E", rest[len(epi):])
         if flags:
             epi += "<" + ",".join(re.findall(r"Lb(\d+)E", flags.group(1))) + ">"
-        return f"gemm {t} {m.group(2)}x{m.group(3)} waves {m.group(4)}x{m.group(5)} {lay} nacc={m.group(8)} {epi}"
+        tag = re.search(r"EELi(\d+)EEEv", n)
+        tag = f" tag {tag.group(1)}" if tag and tag.group(1) != "0" else ""
+        return f"gemm {t} {m.group(2)}x{m.group(3)} waves {m.group(4)}x{m.group(5)} {lay} nacc={m.group(8)} {epi}{tag}"
     return n.split("(")[0].replace("void ", "")
 
 

@@ -32,18 +32,27 @@
  *     statistics and every weight/gain gradient are always fp32.
  *   - Dimensions: T (tokens) >= 1, any value. Every other dimension (d, r,
  *     d_out, ffn, d_shard) must be a positive multiple of 64; G in [1, 16].
- *     Every tensor must be smaller than 2 GiB. Pointers must be 16-byte
- *     aligned.
+ *     Every tensor must be smaller than 2 GiB, and so must every buffer the
+ *     library carves from a workspace (the workspace itself may be larger);
+ *     a descriptor that would need a larger workspace buffer is refused with
+ *     BOOST_ERR_UNSUPPORTED by *_workspace_size and by the call itself.
+ *     Pointers must be 16-byte aligned.
  *   - Ownership: the caller owns every buffer. The library allocates no
  *     device memory, frees nothing, keeps no pointer after return and never
  *     synchronises. Work is enqueued on `stream` (a hipStream_t; NULL = the
  *     default stream) in stream order and runs asynchronously. The backward
- *     calls fork their weight-gradient products onto a side stream (one per
- *     host thread and device, created on first use with the default
- *     priority) through an event recorded on `stream`, and make `stream`
- *     wait for them before returning, so all results are ordered on
- *     `stream` exactly as if everything ran on it; stream capture of
- *     `stream` captures both.
+ *     calls fork their weight-gradient products onto a side stream through
+ *     an event recorded on `stream`, and make `stream` wait for them before
+ *     returning - on every return path, errors included, once anything was
+ *     forked - so all results are ordered on `stream` exactly as if
+ *     everything ran on it; stream capture of `stream` captures both.
+ *   - State: besides the loaded kernels, the library keeps one side stream
+ *     and four events per host thread and device, created on first use
+ *     with the default priority and kept until the process ends (no device
+ *     memory). Two backward calls made from one host thread on different
+ *     streams share that thread's side stream, so their weight-gradient
+ *     products run one after the other (results are unaffected; only the
+ *     overlap between the two calls is lost).
  *   - Outputs are overwritten, never accumulated into. Inputs must not
  *     overlap outputs or the workspace.
  *   - Workspace: `ws` is device scratch of at least the size returned by the

@@ -138,7 +138,18 @@ Choice choose(int dtype, int64_t M, int64_t N, int64_t K, int64_t batch, bool al
   return best;
 }
 
-template <class C, class E>
+// Names of the weight-gradient launches (see gemm_kernel's TAG).
+enum LaunchTag {
+  TAG_NONE = 0,
+  TAG_BLOCK_DB = 1,  // dB of a grouped block (mlp1_dB, lrblock_dB)
+  TAG_BLOCK_DA = 2,  // dA_cat of a grouped block (mlp1_dA, lrblock_dA)
+  TAG_MLP_DB2 = 3,
+  TAG_MLP_DA2 = 4,
+  TAG_BTP_DA = 5,
+  TAG_BTP_DB = 6,
+};
+
+template <class C, class E, int TAG>
 int launch_cfg(const char* label, const Choice& ch, int M, int N, int K, int batch, const GemmOps& ops,
                const typename E::Args& ea, hipStream_t s) {
   GemmGeom g;
@@ -148,29 +159,29 @@ int launch_cfg(const char* label, const Choice& ch, int M, int N, int K, int bat
   if (grid <= 0) return BOOST_OK;
   if (grid > 0x7fffffff) return fail(BOOST_ERR_UNSUPPORTED, "%s: grid too large", label);
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<C, E>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<C, E, TAG>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   (void)attr;
   prof_begin(label, s);
-  hipLaunchKernelGGL((gemm_kernel<C, E>), dim3((unsigned)grid), dim3(C::NT), C::LDS_BYTES, s, g, ops, ea);
+  hipLaunchKernelGGL((gemm_kernel<C, E, TAG>), dim3((unsigned)grid), dim3(C::NT), C::LDS_BYTES, s, g, ops, ea);
   const hipError_t e = hipGetLastError();
   prof_end(s);
   if (e != hipSuccess) return fail(BOOST_ERR_LAUNCH, "%s: %s", label, hipGetErrorString(e));
   return BOOST_OK;
 }
 
-template <class E, bool AKC, bool BKC, int NACC>
+template <class E, bool AKC, bool BKC, int NACC, int TAG = TAG_NONE>
 int gemm(const char* label, int dtype, const Choice& ch, int64_t M, int64_t N, int64_t K, int64_t batch,
          const GemmOps& ops, const typename E::Args& ea, hipStream_t s) {
   const int m = (int)M, n = (int)N, k = (int)K, b = (int)batch;
-  if (dtype == BOOST_DT_F32) return launch_cfg<CF32<AKC, BKC, NACC>, E>(label, ch, m, n, k, b, ops, ea, s);
+  if (dtype == BOOST_DT_F32) return launch_cfg<CF32<AKC, BKC, NACC>, E, TAG>(label, ch, m, n, k, b, ops, ea, s);
   if constexpr (NACC >= 2) {
-    return launch_cfg<C256x128<AKC, BKC, NACC>, E>(label, ch, m, n, k, b, ops, ea, s);
+    return launch_cfg<C256x128<AKC, BKC, NACC>, E, TAG>(label, ch, m, n, k, b, ops, ea, s);
   } else {
     switch (ch.id) {
-      case CFG_256x256: return launch_cfg<C256<AKC, BKC, NACC>, E>(label, ch, m, n, k, b, ops, ea, s);
-      case CFG_256x128: return launch_cfg<C256x128<AKC, BKC, NACC>, E>(label, ch, m, n, k, b, ops, ea, s);
-      default: return launch_cfg<C128<AKC, BKC, NACC>, E>(label, ch, m, n, k, b, ops, ea, s);
+      case CFG_256x256: return launch_cfg<C256<AKC, BKC, NACC>, E, TAG>(label, ch, m, n, k, b, ops, ea, s);
+      case CFG_256x128: return launch_cfg<C256x128<AKC, BKC, NACC>, E, TAG>(label, ch, m, n, k, b, ops, ea, s);
+      default: return launch_cfg<C128<AKC, BKC, NACC>, E, TAG>(label, ch, m, n, k, b, ops, ea, s);
     }
   }
 }
@@ -252,8 +263,10 @@ int launch_act_quant(int dtype, const float* H, void* S, int64_t n, int act, hip
 }
 
 int launch_colsum(const float* part, int P, int64_t stride, int64_t N, float* out, hipStream_t s) {
+  // N <= 2^26 (validated dims), so the grid fits.
+  const int64_t blocks = (N + kColsumCols - 1) / kColsumCols;
   prof_begin("colsum", s);
-  hipLaunchKernelGGL(colsum_kernel, dim3(grid_for(N)), dim3(256), 0, s, part, P, stride, N, out);
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, P, stride, N, out);
   prof_end(s);
   return check_launch("colsum");
 }
@@ -276,6 +289,7 @@ int launch_splitk(int dtype, const float* part, int S, int64_t M, int64_t N, int
 
 // A weight-gradient product out[batch][M][N] (fp32) = rowscale * (A^T-ish @ B)
 // with K = tokens, through split-K partials when the plan asks for them.
+template <int TAG>
 int wgrad(const char* label, int dtype, const Choice& ch, int64_t M, int64_t N, int64_t K, int64_t batch,
           const GemmOps& ops, const void* rowscale, float* out, float* partial, hipStream_t s) {
   EpiStore<true>::Args ea;
@@ -284,27 +298,41 @@ int wgrad(const char* label, int dtype, const Choice& ch, int64_t M, int64_t N, 
     ea.ldo = N;
     ea.pstride = M * N;
     ea.rowscale = nullptr;
-    RBO_TRY((gemm<EpiStore<true>, false, false, 1>(label, dtype, ch, M, N, K, batch, ops, ea, s)));
+    RBO_TRY((gemm<EpiStore<true>, false, false, 1, TAG>(label, dtype, ch, M, N, K, batch, ops, ea, s)));
     return launch_splitk(dtype, partial, ch.splits, M, N, batch, rowscale, out, s);
   }
   ea.out = out;
   ea.ldo = N;
   ea.pstride = M * N;
   ea.rowscale = rowscale;
-  return gemm<EpiStore<true>, false, false, 1>(label, dtype, ch, M, N, K, batch, ops, ea, s);
+  return gemm<EpiStore<true>, false, false, 1, TAG>(label, dtype, ch, M, N, K, batch, ops, ea, s);
 }
 
 // ---------------------------------------------------------------------------
 // Workspace layout
 // ---------------------------------------------------------------------------
+// Sub-buffers are carved at 256-byte offsets. Each sub-buffer is addressed
+// on its own (a buffer resource of at most 2 GiB per GEMM operand), so the
+// 2 GiB limit applies to the largest sub-buffer, not to the workspace.
 struct WsLayout {
   size_t total = 0;
+  size_t largest = 0;
   size_t take(size_t bytes) {
     const size_t off = total;
     total += (bytes + 255) / 256 * 256;
+    largest = std::max(largest, bytes);
     return off;
   }
 };
+
+constexpr size_t kMaxTensorBytes = 0x7fffffff;  // per tensor and per workspace sub-buffer
+
+int check_ws_parts(size_t largest, const char* what) {
+  if (largest >= kMaxTensorBytes)
+    return fail(BOOST_ERR_UNSUPPORTED, "%s workspace needs a %zu-byte buffer; buffers must be smaller than 2 GiB", what,
+                largest);
+  return BOOST_OK;
+}
 
 inline char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
@@ -316,6 +344,7 @@ struct Range {
   size_t bytes;
   const char* name;
   bool out;
+  bool whole = false;  // the workspace: its sub-buffers are checked against the size limit instead
 };
 
 int check_dim64(int64_t v, const char* name) {
@@ -348,7 +377,7 @@ int check_ranges(std::vector<Range>& rs) {
   for (auto& r : rs) {
     if (r.bytes == 0) continue;
     if (!r.p) return fail(BOOST_ERR_INVALID_VALUE, "%s is NULL", r.name);
-    if (r.bytes >= (size_t)0x7fffffff)
+    if (!r.whole && r.bytes >= kMaxTensorBytes)
       return fail(BOOST_ERR_UNSUPPORTED, "%s is %zu bytes; tensors must be smaller than 2 GiB", r.name, r.bytes);
   }
   for (auto& r : rs)
@@ -425,6 +454,45 @@ int stream_after(hipStream_t to, hipStream_t from, Side* sd) {
   return BOOST_OK;
 }
 
+// Fork of the side stream off the caller's stream with a guaranteed join:
+// once a fork has been enqueued, the caller's stream is made to wait for the
+// side stream before the entry point returns, on the success path (join(),
+// whose status is reported) and on every error path (the destructor, which
+// keeps the first error). So whatever a backward returns, work it enqueued
+// on the side stream is ordered before later work on the caller's stream,
+// and a stream capture never ends with the side stream unjoined.
+class SideFork {
+ public:
+  SideFork(Side* sd, hipStream_t main) : sd_(sd), main_(main) {}
+  ~SideFork() {
+    if (forked_) {
+      const std::string keep = g_detail;
+      (void)stream_after(main_, sd_->s, sd_);
+      g_detail = keep;
+    }
+  }
+  SideFork(const SideFork&) = delete;
+  SideFork& operator=(const SideFork&) = delete;
+  hipStream_t side() const { return sd_->s; }
+  // The side stream waits for everything enqueued on the caller's so far.
+  int fork() {
+    RBO_TRY(stream_after(sd_->s, main_, sd_));
+    forked_ = true;
+    return BOOST_OK;
+  }
+  // The caller's stream waits for the side stream.
+  int join() {
+    if (!forked_) return BOOST_OK;
+    forked_ = false;
+    return stream_after(main_, sd_->s, sd_);
+  }
+
+ private:
+  Side* sd_;
+  hipStream_t main_;
+  bool forked_ = false;
+};
+
 // ===========================================================================
 // Grouped block
 // ===========================================================================
@@ -450,6 +518,7 @@ struct LrblockPlan {
   Choice down, up, ds, dB, dA, dx;
   size_t f_AT, f_BT, f_S, f_part, fwd_bytes;
   size_t b_S, b_dU, b_q, b_dg, b_part, bwd_bytes;
+  size_t fwd_largest, bwd_largest;
 };
 
 LrblockPlan lrblock_plan(const boost_lrblock_desc* d) {
@@ -469,6 +538,7 @@ LrblockPlan lrblock_plan(const boost_lrblock_desc* d) {
   // per-tile-column partial row sums of Y^2 (next block's statistic, G = 1)
   p.f_part = G == 1 ? f.take((size_t)(p.up.tiles_n * T * 4)) : 0;
   p.fwd_bytes = f.total;
+  p.fwd_largest = f.largest;
   WsLayout b;
   p.b_S = b.take((size_t)(T * G * r * es));
   p.b_dU = b.take((size_t)(T * G * r * es));
@@ -479,6 +549,7 @@ LrblockPlan lrblock_plan(const boost_lrblock_desc* d) {
   if (p.dA.splits > 1) part = std::max(part, (size_t)(p.dA.splits * D * G * r * 4));
   p.b_part = part ? b.take(part) : 0;
   p.bwd_bytes = b.total;
+  p.bwd_largest = b.largest;
   return p;
 }
 
@@ -542,7 +613,7 @@ int lrblock_bwd_core(int dt, int act, int norm, int64_t T, int64_t D, int64_t r,
                      const float* H, const float* sumsq, const void* dY, void* dx, float* dg, float* dA_cat,
                      float* dB, void* S, bool S_ready, void* dU, float* qpart, float* dgpart, float* partial,
                      const Choice& c_ds, const Choice& c_dB, const Choice& c_dA, const Choice& c_dx,
-                     hipStream_t s, const BwdLabels& L, Side* side, const void* dadd = nullptr) {
+                     hipStream_t s, const BwdLabels& L, SideFork* side, const void* dadd = nullptr) {
   const int64_t es = esize(dt);
   const float inv = norm ? 1.f / (float)d_norm : 0.f;
   // dS_j = dY_j @ B_j^T, fused: dH, dU = rho dH, S = act(H), row partials q.
@@ -560,21 +631,21 @@ int lrblock_bwd_core(int dt, int act, int norm, int64_t T, int64_t D, int64_t r,
   }
   // The weight gradients go to the side stream (it waits for dS, which
   // produces dU and, here, S); dx stays on the caller's stream.
-  const hipStream_t sw = side ? side->s : s;
-  if (side) RBO_TRY(stream_after(sw, s, side));
+  const hipStream_t sw = side ? side->side() : s;
+  if (side) RBO_TRY(side->fork());
   // dB_j = S_j^T @ dY_j  (K = T).
   {
     GemmOps ops{};
     ops.a[0] = opnd(S, G * r, T, r, es, r);
     ops.b[0] = opnd(dY, n, T, n, es, T * n);
-    RBO_TRY(wgrad(L.dB, dt, c_dB, r, n, T, G, ops, nullptr, dB, partial, sw));
+    RBO_TRY(wgrad<TAG_BLOCK_DB>(L.dB, dt, c_dB, r, n, T, G, ops, nullptr, dB, partial, sw));
   }
   // dA_cat = diag(g) (x^T @ dU)  (K = T); the gain row scale is exact in fp32.
   {
     GemmOps ops{};
     ops.a[0] = opnd(x, D, T, D, es);
     ops.b[0] = opnd(dU, G * r, T, G * r, es);
-    RBO_TRY(wgrad(L.dA, dt, c_dA, D, G * r, T, 1, ops, norm ? g : nullptr, dA_cat, partial, sw));
+    RBO_TRY(wgrad<TAG_BLOCK_DA>(L.dA, dt, c_dA, D, G * r, T, 1, ops, norm ? g : nullptr, dA_cat, partial, sw));
   }
   // dx~ = dU @ A_cat^T, fused with the RMSNorm backward and dg partials.
   {
@@ -591,7 +662,7 @@ int lrblock_bwd_core(int dt, int act, int norm, int64_t T, int64_t D, int64_t r,
     }
   }
   // Join: the caller's stream waits for the weight gradients.
-  if (side) RBO_TRY(stream_after(s, sw, side));
+  if (side) RBO_TRY(side->join());
   return BOOST_OK;
 }
 
@@ -618,6 +689,7 @@ struct LrmlpPlan {
   Choice ds2, dB2, rec, dA2, ds1, dB1, dA1, dx1;        // backward
   size_t f_A1T, f_B1T, f_A2T, f_B2T, f_S1, f_M, f_S2, f_part, fwd_bytes;
   size_t b_B1T, b_S2, b_dU2, b_S1, b_M, b_dY, b_dU1, b_q, b_dg, b_part, bwd_bytes;
+  size_t fwd_largest, bwd_largest;
 };
 
 LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
@@ -646,6 +718,7 @@ LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
   p.f_S2 = f.take((size_t)(T * r * es));
   p.f_part = f.take((size_t)(p.up2.tiles_n * T * 4));  // next block's statistic partials
   p.fwd_bytes = f.total;
+  p.fwd_largest = f.largest;
   WsLayout b;
   p.b_B1T = b.take((size_t)(2 * r * F * es));
   p.b_S2 = b.take((size_t)(T * r * es));
@@ -663,6 +736,7 @@ LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
   if (p.dA1.splits > 1) part = std::max(part, (size_t)(p.dA1.splits * D * 2 * r * 4));
   p.b_part = part ? b.take(part) : 0;
   p.bwd_bytes = b.total;
+  p.bwd_largest = b.largest;
   return p;
 }
 
@@ -686,6 +760,7 @@ struct BtpPlan {
   // dA_s and dB_s run on different streams, so their split-K partials get
   // separate buffers.
   size_t b_BT, b_du, b_ag, b_dg, b_part_dA, b_part_dB, bwd_bytes;
+  size_t fwd_largest, bwd_largest;
 };
 
 BtpPlan btp_plan(const boost_btp_share_desc* d) {
@@ -704,6 +779,7 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   p.f_ag = f.take((size_t)(T * S * es));
   p.f_sp = f.take((size_t)(p.u.tiles_n * T * 4));
   p.fwd_bytes = f.total;
+  p.fwd_largest = f.largest;
   WsLayout b;
   p.b_BT = b.take((size_t)(r * S * es));
   p.b_du = b.take((size_t)(T * S * es));
@@ -712,6 +788,7 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   p.b_part_dA = p.dA.splits > 1 ? b.take((size_t)(p.dA.splits * S * r * 4)) : 0;
   p.b_part_dB = p.dB.splits > 1 ? b.take((size_t)(p.dB.splits * r * S * 4)) : 0;
   p.bwd_bytes = b.total;
+  p.bwd_largest = b.largest;
   return p;
 }
 
@@ -749,6 +826,7 @@ int boost_lrblock_workspace_size(const boost_lrblock_desc* d, int is_bwd, size_t
   RBO_TRY(lrblock_check_desc(d));
   if (!bytes) return fail(BOOST_ERR_INVALID_VALUE, "bytes is NULL");
   const LrblockPlan p = lrblock_plan(d);
+  RBO_TRY(check_ws_parts(is_bwd ? p.bwd_largest : p.fwd_largest, is_bwd ? "backward" : "forward"));
   *bytes = is_bwd ? p.bwd_bytes : p.fwd_bytes;
   return BOOST_OK;
 }
@@ -775,9 +853,10 @@ int boost_lrblock_fwd_chained(const boost_lrblock_desc* d, const void* x, const 
       {H, T * G * r * 4, "H", true},
       {sumsq, d->norm && (!sumsq_in || sumsq) ? T * 4 : 0, "sumsq", true},
       {sumsq_next, sumsq_next ? T * 4 : 0, "sumsq_next", true},
-      {ws, (ws && p.fwd_bytes <= ws_bytes) ? p.fwd_bytes : 0, "ws", true},
+      {ws, (ws && p.fwd_bytes <= ws_bytes) ? p.fwd_bytes : 0, "ws", true, true},
   };
   RBO_TRY(check_ranges(rs));
+  RBO_TRY(check_ws_parts(p.fwd_largest, "forward"));
   RBO_TRY(check_ws(ws, ws_bytes, p.fwd_bytes));
   return lrblock_fwd_impl(d, x, g, A_cat, B, residual, sumsq_in, Y, H, sumsq, sumsq_next, ws, as_stream(stream));
 }
@@ -810,18 +889,20 @@ int boost_lrblock_bwd_chained(const boost_lrblock_desc* d, const void* x, const 
       {dg, d->norm ? D * 4 : 0, "dg", true},
       {dA_cat, D * G * r * 4, "dA_cat", true},
       {dB, G * r * n * 4, "dB", true},
-      {ws, (ws && p.bwd_bytes <= ws_bytes) ? p.bwd_bytes : 0, "ws", true},
+      {ws, (ws && p.bwd_bytes <= ws_bytes) ? p.bwd_bytes : 0, "ws", true, true},
   };
   RBO_TRY(check_ranges(rs));
+  RBO_TRY(check_ws_parts(p.bwd_largest, "backward"));
   RBO_TRY(check_ws(ws, ws_bytes, p.bwd_bytes));
-  Side* side = nullptr;
-  RBO_TRY(side_for_device(&side));
+  Side* sd = nullptr;
+  RBO_TRY(side_for_device(&sd));
+  SideFork side(sd, as_stream(stream));
   return lrblock_bwd_core(d->dtype, d->act, d->norm, d->T, d->d, d->r, d->G, d->d_out, d->eps, d->d_norm, x, g,
                           A_cat, B, H, sumsq, dY, dx, dg, dA_cat, dB, at(ws, p.b_S), false, at(ws, p.b_dU),
                           d->norm ? reinterpret_cast<float*>(at(ws, p.b_q)) : nullptr,
                           d->norm ? reinterpret_cast<float*>(at(ws, p.b_dg)) : nullptr,
                           p.b_part ? reinterpret_cast<float*>(at(ws, p.b_part)) : nullptr, p.ds, p.dB, p.dA, p.dx,
-                          as_stream(stream), kLrblockLabels, side, dx_add);
+                          as_stream(stream), kLrblockLabels, &side, dx_add);
 }
 
 int boost_lrblock_bwd(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat, const void* B,
@@ -837,6 +918,7 @@ int boost_lrmlp_workspace_size(const boost_lrmlp_desc* d, int is_bwd, size_t* by
   RBO_TRY(lrmlp_check_desc(d));
   if (!bytes) return fail(BOOST_ERR_INVALID_VALUE, "bytes is NULL");
   const LrmlpPlan p = lrmlp_plan(d);
+  RBO_TRY(check_ws_parts(is_bwd ? p.bwd_largest : p.fwd_largest, is_bwd ? "backward" : "forward"));
   *bytes = is_bwd ? p.bwd_bytes : p.fwd_bytes;
   return BOOST_OK;
 }
@@ -865,9 +947,10 @@ int boost_lrmlp_fwd_chained(const boost_lrmlp_desc* d, const void* x, const void
       {H2, (size_t)(T * r) * 4, "H2", true},
       {sumsq, (!sumsq_in || sumsq) ? (size_t)T * 4 : 0, "sumsq", true},
       {sumsq_next, sumsq_next ? (size_t)T * 4 : 0, "sumsq_next", true},
-      {ws, (ws && p.fwd_bytes <= ws_bytes) ? p.fwd_bytes : 0, "ws", true},
+      {ws, (ws && p.fwd_bytes <= ws_bytes) ? p.fwd_bytes : 0, "ws", true, true},
   };
   RBO_TRY(check_ranges(rs));
+  RBO_TRY(check_ws_parts(p.fwd_largest, "forward"));
   RBO_TRY(check_ws(ws, ws_bytes, p.fwd_bytes));
   hipStream_t s = as_stream(stream);
   void* A1T = at(ws, p.f_A1T);
@@ -966,9 +1049,10 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void
       {dB1, (size_t)(2 * r * F) * 4, "dB1", true},
       {dA2, (size_t)(F * r) * 4, "dA2", true},
       {dB2, (size_t)(r * D) * 4, "dB2", true},
-      {ws, (ws && p.bwd_bytes <= ws_bytes) ? p.bwd_bytes : 0, "ws", true},
+      {ws, (ws && p.bwd_bytes <= ws_bytes) ? p.bwd_bytes : 0, "ws", true, true},
   };
   RBO_TRY(check_ranges(rs));
+  RBO_TRY(check_ws_parts(p.bwd_largest, "backward"));
   RBO_TRY(check_ws(ws, ws_bytes, p.bwd_bytes));
   hipStream_t s = as_stream(stream);
   void* S2 = at(ws, p.b_S2);
@@ -980,8 +1064,9 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void
   float* q = reinterpret_cast<float*>(at(ws, p.b_q));
   float* dgp = reinterpret_cast<float*>(at(ws, p.b_dg));
   float* part = p.b_part ? reinterpret_cast<float*>(at(ws, p.b_part)) : nullptr;
-  Side* side = nullptr;
-  RBO_TRY(side_for_device(&side));
+  Side* sd = nullptr;
+  RBO_TRY(side_for_device(&sd));
+  SideFork side(sd, s);
   {  // dS2 = dY @ B2^T; dU2 = dS2 * act'(H2); S2 = act(H2)
     GemmOps ops{};
     ops.a[0] = opnd(dY, D, T, D, es);
@@ -990,12 +1075,12 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void
     RBO_TRY((gemm<EpiDS<false>, true, true, 1>("mlp_ds2", dt, p.ds2, T, r, D, 1, ops, ea, s)));
   }
   // Weight gradients on the side stream, each after what it reads is ready.
-  RBO_TRY(stream_after(side->s, s, side));
+  RBO_TRY(side.fork());
   {  // dB2 = S2^T @ dY
     GemmOps ops{};
     ops.a[0] = opnd(S2, r, T, r, es);
     ops.b[0] = opnd(dY, D, T, D, es);
-    RBO_TRY(wgrad("mlp_dB2", dt, p.dB2, r, D, T, 1, ops, nullptr, dB2, part, side->s));
+    RBO_TRY(wgrad<TAG_MLP_DB2>("mlp_dB2", dt, p.dB2, r, D, T, 1, ops, nullptr, dB2, part, side.side()));
   }
   // S1 = act(H1) recomputed from the saved bottleneck.
   RBO_TRY(launch_act_quant(dt, H1, S1, T * 2 * r, d->act, s));
@@ -1012,18 +1097,18 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void
     EpiSwigluBwd::Args ea{Mr, dYgu, F, T * F};
     RBO_TRY((gemm<EpiSwigluBwd, true, true, 3>("mlp_recompute_swiglu_bwd", dt, p.rec, T, F, r, 1, ops, ea, s)));
   }
-  RBO_TRY(stream_after(side->s, s, side));
+  RBO_TRY(side.fork());
   {  // dA2 = M^T @ dU2
     GemmOps ops{};
     ops.a[0] = opnd(Mr, F, T, F, es);
     ops.b[0] = opnd(dU2, r, T, r, es);
-    RBO_TRY(wgrad("mlp_dA2", dt, p.dA2, F, r, T, 1, ops, nullptr, dA2, part, side->s));
+    RBO_TRY(wgrad<TAG_MLP_DA2>("mlp_dA2", dt, p.dA2, F, r, T, 1, ops, nullptr, dA2, part, side.side()));
   }
   // Block 1 backward with dY = (dYg, dYu); S1 already recomputed. It joins
   // the side stream back into the caller's before returning.
   return lrblock_bwd_core(dt, d->act, 1, T, D, r, 2, F, d->eps, D, x, g, A1_cat, B1, H1, sumsq, dYgu, dx, dg,
                           dA1_cat, dB1, S1, true, dU1, q, dgp, part, p.ds1, p.dB1, p.dA1, p.dx1, s, kMlp1Labels,
-                          side, dx_add);
+                          &side, dx_add);
 }
 
 int boost_lrmlp_bwd(const boost_lrmlp_desc* d, const void* x, const void* g, const void* A1_cat, const void* B1,
@@ -1040,6 +1125,7 @@ int boost_btp_share_workspace_size(const boost_btp_share_desc* d, int is_bwd, si
   RBO_TRY(btp_check_desc(d));
   if (!bytes) return fail(BOOST_ERR_INVALID_VALUE, "bytes is NULL");
   const BtpPlan p = btp_plan(d);
+  RBO_TRY(check_ws_parts(is_bwd ? p.bwd_largest : p.fwd_largest, is_bwd ? "backward" : "forward"));
   *bytes = is_bwd ? p.bwd_bytes : p.fwd_bytes;
   return BOOST_OK;
 }
@@ -1059,9 +1145,10 @@ int boost_btp_share_fwd(const boost_btp_share_desc* d, const void* z, const void
       {A_s, (size_t)(S * r) * es, "A_s", false},
       {pout, (size_t)(T * r) * es, "p", true},
       {s_out, (size_t)T * 4, "s", true},
-      {ws, (ws && p.fwd_bytes <= ws_bytes) ? p.fwd_bytes : 0, "ws", true},
+      {ws, (ws && p.fwd_bytes <= ws_bytes) ? p.fwd_bytes : 0, "ws", true, true},
   };
   RBO_TRY(check_ranges(rs));
+  RBO_TRY(check_ws_parts(p.fwd_largest, "forward"));
   RBO_TRY(check_ws(ws, ws_bytes, p.fwd_bytes));
   hipStream_t st = as_stream(stream);
   void* BT = at(ws, p.f_BT);
@@ -1106,9 +1193,10 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
       {dB_s, (size_t)(r * S) * 4, "dB_s", true},
       {dg_s, (size_t)S * 4, "dg_s", true},
       {dA_s, (size_t)(S * r) * 4, "dA_s", true},
-      {ws, (ws && p.bwd_bytes <= ws_bytes) ? p.bwd_bytes : 0, "ws", true},
+      {ws, (ws && p.bwd_bytes <= ws_bytes) ? p.bwd_bytes : 0, "ws", true, true},
   };
   RBO_TRY(check_ranges(rs));
+  RBO_TRY(check_ws_parts(p.bwd_largest, "backward"));
   RBO_TRY(check_ws(ws, ws_bytes, p.bwd_bytes));
   hipStream_t st = as_stream(stream);
   void* du = at(ws, p.b_du);
@@ -1130,14 +1218,15 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
   RBO_TRY(launch_colsum(dgp, p.ue.tiles_m, S, S, dg_s, st));
   // dA_s on the side stream; dz, then dB_s, on the caller's (two weight
   // gradients in a row on the side stream would finish well after dz).
-  Side* side = nullptr;
-  RBO_TRY(side_for_device(&side));
-  RBO_TRY(stream_after(side->s, st, side));
+  Side* sd = nullptr;
+  RBO_TRY(side_for_device(&sd));
+  SideFork side(sd, st);
+  RBO_TRY(side.fork());
   {  // dA_s = ag^T @ dp
     GemmOps ops{};
     ops.a[0] = opnd(ag, S, T, S, es);
     ops.b[0] = opnd(dp, r, T, r, es);
-    RBO_TRY(wgrad("btp_dA", dt, p.dA, S, r, T, 1, ops, nullptr, dA_s, part_dA, side->s));
+    RBO_TRY(wgrad<TAG_BTP_DA>("btp_dA", dt, p.dA, S, r, T, 1, ops, nullptr, dA_s, part_dA, side.side()));
   }
   {  // dz = du @ B_s^T
     GemmOps ops{};
@@ -1150,10 +1239,9 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);
     ops.b[0] = opnd(du, S, T, S, es);
-    RBO_TRY(wgrad("btp_dB", dt, p.dB, r, S, T, 1, ops, nullptr, dB_s, part_dB, st));
+    RBO_TRY(wgrad<TAG_BTP_DB>("btp_dB", dt, p.dB, r, S, T, 1, ops, nullptr, dB_s, part_dB, st));
   }
-  RBO_TRY(stream_after(st, side->s, side));
-  return BOOST_OK;
+  return side.join();
 }
 
 // ------------------------------- profiler ---------------------------------

@@ -515,7 +515,10 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <class C, class E>
+// TAG only names the instantiation: launches that would otherwise share a
+// kernel (the weight-gradient products) get distinct symbols, so a profiler
+// can attribute each one.
+template <class C, class E, int TAG = 0>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, typename E::Args ea) {
   typedef typename C::T T;
   typedef Mfma<T> MF;

@@ -242,3 +242,39 @@ def test_binding_checks_operands_against_the_descriptor():
     with pytest.raises(ValueError, match="GPU"):
         binding._anchor(x, "x")
     assert binding._nbytes(torch.zeros(10, dtype=torch.float32)) == 40
+
+
+def test_workspace_limit_applies_per_buffer_not_to_the_whole_workspace(B):
+    """Each buffer carved from a workspace is addressed on its own, so only
+    those buffers (and every tensor) must stay below 2 GiB: the 40B-shaped
+    MLP backward at T = 16384 needs a workspace above 2 GiB and is accepted
+    (the call goes on to the workspace-size check), while a descriptor whose
+    largest workspace buffer reaches 2 GiB, or a tensor of 2 GiB, is refused."""
+    E_UNS, E_WS = 2, 5
+    L = B.lib()
+    d, r, ffn = 8192, 2048, 22016
+    desc = B.lrmlp_desc(16384, d, r, ffn, B.DT_BF16)
+    need = B.lrmlp_workspace_size(desc, True)
+    assert need > (1 << 31)
+    f = Fake()
+    T = desc.T
+    es = 2
+    ins = [f(T * d * es), f(d * es), f(d * 2 * r * es), f(2 * r * ffn * es), f(ffn * r * es), f(r * d * es),
+           f(T * 2 * r * 4), f(T * r * 4), f(T * 4), f(T * d * es)]
+    outs = [f(T * d * es), f(d * 4), f(d * 2 * r * 4), f(2 * r * ffn * 4), f(ffn * r * 4), f(r * d * 4)]
+    ws = f(need)
+    assert L.boost_lrmlp_bwd(ctypes.byref(desc), *ins, *outs, ws, need - 256, None) == E_WS
+    assert b"workspace of" in L.boost_last_error_detail()
+    # T = 32768: every tensor is below 2 GiB, but the [2, T, ffn] gradient
+    # buffer of the workspace is 2.9 GB
+    big = B.lrmlp_desc(32768, d, r, ffn, B.DT_BF16)
+    n = ctypes.c_size_t(0)
+    assert L.boost_lrmlp_workspace_size(ctypes.byref(big), 1, ctypes.byref(n)) == E_UNS
+    assert b"smaller than 2 GiB" in L.boost_last_error_detail()
+    # a 2 GiB input tensor is refused
+    huge = B.lrmlp_desc(131072, d, r, ffn, B.DT_BF16)
+    T = huge.T
+    ins = [f(T * d * es)] + ins[1:6] + [f(T * 2 * r * 4), f(T * r * 4), f(T * 4), f(T * d * es)]
+    outs = [f(T * d * es)] + outs[1:]
+    assert L.boost_lrmlp_bwd(ctypes.byref(huge), *ins, *outs, f(1 << 20), 1 << 20, None) == E_UNS
+    assert b"x is" in L.boost_last_error_detail()

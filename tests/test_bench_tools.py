@@ -18,11 +18,11 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 from rank_bottleneck_online_amd import synth  # noqa: E402
 
-SWIGLU_BWD = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi256ELi128ELi4ELi2ELb1ELb1ELi3EEENS_12EpiSwigluBwdEEEvNS_8"
+SWIGLU_BWD = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi256ELi128ELi4ELi2ELb1ELb1ELi3EEENS_12EpiSwigluBwdELi0EEEvNS_8"
               "GemmGeomENS_7GemmOpsENT0_4ArgsE")
-DOWN1 = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi256ELi256ELi2ELi4ELb1ELb1ELi1EEENS_7EpiDownILb1ELb0EEEEEvNS_8"
+DOWN1 = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi256ELi256ELi2ELi4ELb1ELb1ELi1EEENS_7EpiDownILb1ELb0EEELi0EEEvNS_8"
          "GemmGeomENS_7GemmOpsENT0_4ArgsE")
-WGRAD = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi128ELi128ELi2ELi4ELb0ELb0ELi1EEENS_8EpiStoreILb1EEEEEvNS_8"
+WGRAD = ("_ZN3rbo11gemm_kernelINS_3CfgIDF16bLi128ELi128ELi2ELi4ELb0ELb0ELi1EEENS_8EpiStoreILb1EEELi4EEEvNS_8"
          "GemmGeomENS_7GemmOpsENT0_4ArgsE")
 
 
@@ -54,8 +54,19 @@ def test_lrblock_backward_is_twice_the_forward():
 def test_short_kernel_names():
     assert bench.short_kernel_name(SWIGLU_BWD) == "gemm bf16 256x128 waves 4x2 KC/KC nacc=3 EpiSwigluBwd"
     assert bench.short_kernel_name(DOWN1) == "gemm bf16 256x256 waves 2x4 KC/KC nacc=1 EpiDown<1,0>"
-    assert bench.short_kernel_name(WGRAD) == "gemm bf16 128x128 waves 2x4 MC/NC nacc=1 EpiStore<1>"
+    assert bench.short_kernel_name(WGRAD) == "gemm bf16 128x128 waves 2x4 MC/NC nacc=1 EpiStore<1> tag 4"
     assert bench.short_kernel_name("void rbo::colsum_kernel(float const*)") == "rbo::colsum_kernel"
+
+
+def test_each_mlp_label_names_one_kernel():
+    """Every launch label of the MLP step maps to exactly one of the step's
+    kernel instantiations (the weight-gradient products carry a launch tag)."""
+    names = [SWIGLU_BWD, DOWN1, WGRAD]
+    for tag in (1, 2, 3):
+        names.append(WGRAD.replace("EELi4EEEv", f"EELi{tag}EEEv"))
+    for lab in ("mlp1_dB", "mlp1_dA", "mlp_dB2", "mlp_dA2", "mlp_recompute_swiglu_bwd", "mlp_down1"):
+        hits = [n for n in names if bench.MLP_LABEL_PATTERNS[lab] in n]
+        assert len(hits) == 1, (lab, hits)
 
 
 def _counter_csv(path, rows):
