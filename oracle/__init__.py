@@ -11,6 +11,7 @@ from .lrblock import (  # noqa: F401
     act_fn,
     act_grad,
     btp_consumer,
+    btp_consumer_backward,
     btp_share_backward,
     btp_share_forward,
     lrblock_backward,

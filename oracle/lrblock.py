@@ -288,3 +288,17 @@ def btp_consumer(p_parts, s_parts, eps, d_norm):
     S = np.sum(np.stack(s_parts), axis=0)
     rho = 1.0 / np.sqrt(S / d_norm + eps)
     return rho[:, None] * P, rho, P
+
+
+def btp_consumer_backward(dz_next, rho, Psum, d_norm):
+    """Gradients of every share's own outputs from the consumer's output
+    gradient dz_next (BOOST summary, technical summary 2.1 and 2.2: each rank
+    forms them locally, with no exchange). From z_next = rho * Psum and
+    rho = (S / d_norm + eps)^(-1/2) with S = sum_p s_p:
+      dp = rho * dz_next                            (the same for every share)
+      ds = d rho / d S * <dz_next, Psum>_row = -(rho^3 / (2 d_norm)) <dz_next, Psum>_row
+    """
+    dz_next = np.asarray(dz_next, np.float64)
+    dp = rho[:, None] * dz_next
+    ds = -(rho ** 3) / (2.0 * d_norm) * np.sum(dz_next * Psum, axis=1)
+    return dp, ds

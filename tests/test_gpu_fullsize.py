@@ -55,11 +55,21 @@ def test_llama2_7b_mlp_fwd_bwd(B):
 
 
 def test_llama2_13b_btp_share_tp4(B):
+    """Share 0 of four at the 13B shape. Its backward inputs come from the
+    fp64 simulation of all four shares and the consumer that sums them:
+    dp = rho * dz_next and ds from the chain rule through rho (what a rank
+    forms locally), rounded to their storage types (bf16, fp32)."""
     w = synth.WORKLOADS["llama2_13b_btp_share_tp4"]
     T, r, D, P = w["T"], w["r"], w["d_global"], w["P"]
     say(f"full-size 13B BTP share T={T} r={r} d_global={D} P={P}")
     inp = synth.btp_inputs(T, r, D, P, dtype="bf16", seed=0)
-    sh = synth.btp_shard(inp, 0, P)
+    shards = [synth.btp_shard(inp, p, P) for p in range(P)]
+    names = ("z", "B_s", "g_s", "A_s")
+    fw = [oracle.btp_share_forward(*(s[k] for k in names)) for s in shards]
+    _, rho, Psum = oracle.btp_consumer([f["p"] for f in fw], [f["s"] for f in fw], 1e-5, D)
+    dp, ds = oracle.btp_consumer_backward(inp["dz_next"], rho, Psum, D)
+    sh = dict(shards[0], dp=oracle.round_to_bf16(dp), ds=synth.round_to_f32(ds))
+    say(f"  simulated dp: rms {np.sqrt(np.mean(sh['dp'] ** 2)):.3e}; ds: rms {np.sqrt(np.mean(sh['ds'] ** 2)):.3e}")
     out = run_btp(B, sh, "bf16")
     args = [sh[k] for k in ("z", "B_s", "g_s", "A_s")]
     ref = oracle.btp_share_forward(*args)

@@ -360,8 +360,7 @@ def test_btp_shards_reproduce_unsharded_pair():
     assert rel(sum(f["s"] for f in fw), ref["sumsq"]) < 1e-13
 
     # Backward: the gradients of one share's outputs are local (no exchange).
-    dp = rho[:, None] * dz_next
-    ds = -(rho ** 3) / (2.0 * D) * np.sum(dz_next * Psum, axis=1)
+    dp, ds = oracle.btp_consumer_backward(dz_next, rho, Psum, D)
     bw = [oracle.btp_share_backward(**s, dp=dp, ds=ds) for s in shards]
     ub = oracle.lrblock_backward(a, g_full, A_full, np.eye(r)[None], dz_next[None],
                                  act="identity", norm=True, eps=eps, d_norm=D)
