@@ -129,6 +129,22 @@ int boost_lrblock_fwd(const boost_lrblock_desc* desc, const void* x, const void*
                       const void* A_cat, const void* B, void* Y, float* H, float* sumsq,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* The forward above with no workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation). Its scratch (transposed weights and
+ * act(H)) lives in a fixed 64 MiB array that the library holds on each
+ * device it runs on until the process ends; it calls no allocator. A
+ * descriptor whose forward workspace (boost_lrblock_workspace_size with
+ * is_bwd = 0) exceeds 64 MiB is refused with BOOST_ERR_UNSUPPORTED (the
+ * 1B-shaped QKV forward, T = 16384, d = 2048, r = 512, G = 3, needs 60 MiB).
+ * Every call on a device shares that device's array: calls that may overlap
+ * on one device (different streams, different host threads) race and give
+ * undefined results; serialise them. Nothing in the scratch needs to start
+ * at zero. Results are bit-identical to boost_lrblock_fwd. */
+int boost_lrblock_fwd_noalloc(const boost_lrblock_desc* desc, const void* x, const void* g,
+                              const void* A_cat, const void* B, void* Y, float* H, float* sumsq,
+                              void* stream);
+
 /* Backward with low-rank activation checkpointing (section 2.2): from the
  * inputs, the saved H and sumsq, and dY[G,T,d_out] (dtype) only; act(H),
  * act'(H) and rho are recomputed. Outputs: dx[T,d] (dtype), dg[d] fp32 (NULL

@@ -57,6 +57,7 @@ _SIGS = {
     "boost_lrblock_workspace_size": ([ctypes.POINTER(LrblockDesc), ctypes.c_int, ctypes.POINTER(_SZ)], ctypes.c_int),
     "boost_lrblock_fwd": ([ctypes.POINTER(LrblockDesc)] + [_VP] * 7 + [_VP, _SZ, _VP], ctypes.c_int),
     "boost_lrblock_bwd": ([ctypes.POINTER(LrblockDesc)] + [_VP] * 11 + [_VP, _SZ, _VP], ctypes.c_int),
+    "boost_lrblock_fwd_noalloc": ([ctypes.POINTER(LrblockDesc)] + [_VP] * 7 + [_VP], ctypes.c_int),
     "boost_lrmlp_workspace_size": ([ctypes.POINTER(LrmlpDesc), ctypes.c_int, ctypes.POINTER(_SZ)], ctypes.c_int),
     "boost_lrmlp_fwd": ([ctypes.POINTER(LrmlpDesc)] + [_VP] * 10 + [_VP, _SZ, _VP], ctypes.c_int),
     "boost_lrmlp_bwd": ([ctypes.POINTER(LrmlpDesc)] + [_VP] * 16 + [_VP, _SZ, _VP], ctypes.c_int),
@@ -304,6 +305,27 @@ def lrblock_fwd(x, g, A_cat, B, act="silu", norm=True, eps=1e-5, d_norm=None, ou
     _check(lib().boost_lrblock_fwd(ctypes.byref(desc), _ptr(x), _ptr(g) if norm else None, _ptr(A_cat), _ptr(B),
                                    _ptr(Y), _ptr(H), _ptr(sumsq), _ptr(ws), _nbytes(ws), _stream(stream)),
            "boost_lrblock_fwd")
+    return Y, H, sumsq
+
+
+def lrblock_fwd_noalloc(x, g, A_cat, B, act="silu", norm=True, eps=1e-5, d_norm=None, out=None, stream=None):
+    """The forward with the library's fixed scratch instead of a workspace;
+    `out` = (Y, H, sumsq) must be given (nothing is allocated here)."""
+    _anchor(x, "x")
+    T, d = x.shape
+    G, r, d_out = B.shape
+    _block_args(x, g, A_cat, B, norm)
+    desc = lrblock_desc(T, d, r, G, d_out, _dtype_code(x), act, norm, eps, d_norm)
+    if out is None:
+        raise ValueError("lrblock_fwd_noalloc needs preallocated outputs (Y, H, sumsq)")
+    Y, H, sumsq = out
+    _arg(Y, (G, T, d_out), x.dtype, x, "Y")
+    _arg(H, (T, G * r), F32, x, "H")
+    if norm:
+        _arg(sumsq, (T,), F32, x, "sumsq")
+    _check(lib().boost_lrblock_fwd_noalloc(ctypes.byref(desc), _ptr(x), _ptr(g) if norm else None, _ptr(A_cat),
+                                           _ptr(B), _ptr(Y), _ptr(H), _ptr(sumsq), _stream(stream)),
+           "boost_lrblock_fwd_noalloc")
     return Y, H, sumsq
 
 

@@ -14,6 +14,7 @@
 #include <cstring>
 #include <string>
 #include <initializer_list>
+#include <mutex>
 #include <vector>
 
 #include "../../include/boost_lrblock.h"
@@ -792,6 +793,35 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   return p;
 }
 
+// ---------------------------------------------------------------------------
+// Fixed scratch for the forward that allocates nothing. Each device that
+// loads the library holds one copy of this array until the process ends; a
+// host-side reference to `scratch` is only a stand-in, so its device address
+// is looked up once per device (with that device current) and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BOOST_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDev) return fail(BOOST_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(BOOST_ERR_LAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return BOOST_OK;
+}
+
 }  // namespace
 }  // namespace rbo
 
@@ -864,6 +894,34 @@ int boost_lrblock_fwd_chained(const boost_lrblock_desc* d, const void* x, const 
 int boost_lrblock_fwd(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat, const void* B,
                       void* Y, float* H, float* sumsq, void* ws, size_t ws_bytes, void* stream) {
   return boost_lrblock_fwd_chained(d, x, g, A_cat, B, nullptr, nullptr, Y, H, sumsq, nullptr, ws, ws_bytes, stream);
+}
+
+int boost_lrblock_fwd_noalloc(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat,
+                              const void* B, void* Y, float* H, float* sumsq, void* stream) {
+  g_detail.clear();
+  RBO_TRY(lrblock_check_desc(d));
+  const size_t es = esize(d->dtype);
+  const size_t T = d->T, D = d->d, r = d->r, G = d->G, n = d->d_out;
+  const LrblockPlan p = lrblock_plan(d);
+  std::vector<Range> rs = {
+      {x, T * D * es, "x", false},
+      {g, d->norm ? D * es : 0, "g", false},
+      {A_cat, D * G * r * es, "A_cat", false},
+      {B, G * r * n * es, "B", false},
+      {Y, G * T * n * es, "Y", true},
+      {H, T * G * r * 4, "H", true},
+      {sumsq, d->norm ? T * 4 : 0, "sumsq", true},
+  };
+  RBO_TRY(check_ranges(rs));
+  if (p.fwd_bytes > kNoAllocScratchBytes)
+    return fail(BOOST_ERR_UNSUPPORTED, "needs %zu bytes of scratch; the fixed scratch holds %zu", p.fwd_bytes,
+                kNoAllocScratchBytes);
+  void* ws = nullptr;
+  RBO_TRY(noalloc_scratch(&ws));
+  // The scratch is the library's own memory; no caller tensor may lie in it.
+  rs.push_back({ws, p.fwd_bytes, "scratch", true});
+  RBO_TRY(check_ranges(rs));
+  return lrblock_fwd_impl(d, x, g, A_cat, B, nullptr, nullptr, Y, H, sumsq, nullptr, ws, as_stream(stream));
 }
 
 int boost_lrblock_bwd_chained(const boost_lrblock_desc* d, const void* x, const void* g, const void* A_cat,
