@@ -297,8 +297,8 @@ struct DirectLoaderMN {
   static_assert(C::BK % (RPI * C::NW) == 0, "direct loader: rows must split evenly over the waves");
   // k0: first k row of the slab (relative to the operand base); oob as for
   // the K-contiguous loader.
-  __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int k0, char* tile,
-                                               int wave, int lane, uint32_t oob = 0) {
+  __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int k0,
+                                               char* __restrict__ tile, int wave, int lane, uint32_t oob = 0) {
 #pragma unroll
     for (int q = 0; q < INSTR; ++q) {
       const int row0 = RPI * (q * C::NW + wave);
@@ -320,7 +320,12 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 template <class C, int RS>
 struct MnFrag {
   typedef typename Mfma<typename C::T>::Frag Frag;
-  __device__ __forceinline__ static Frag read(const char* tile, int c0, int k0, int lane) {
+  // `tile` is restrict-qualified, as is the destination of the direct-to-LDS
+  // loads: the stage read here is never the one being filled (the slab
+  // pipeline waits for a stage's loads before its first read), and without
+  // that promise the compiler waits for every LDS-bound load in flight
+  // before each transposing read.
+  __device__ __forceinline__ static Frag read(const char* __restrict__ tile, int c0, int k0, int lane) {
     if constexpr (C::ES == 2) {
       // ds_read_b64_tr_b16: in each group g of 16 lanes, source lane j reads
       // 4 consecutive columns at one k row, and lane i receives component
@@ -639,12 +644,16 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
   };
 
   constexpr int L = DA::INSTR + DB::INSTR;  // loads per wave per K slab
-  // The compiler cannot tell the transposing LDS reads apart from the
-  // slab being loaded into another stage, and waits for every load in
-  // flight before each of them. With an M/N-major operand the next slab is
-  // therefore issued in the last sub-step, after the stage's last reads.
-  typedef std::conditional_t<C::AKC && C::BKC, SlabPlan<DA::INSTR, 0, DB::INSTR, 1>,
-                             SlabPlan<DA::INSTR, KK - 1, DB::INSTR, KK - 1>> Plan;
+  // The next slab's loads go out during the first two sub-steps (the
+  // restrict-qualified LDS pointers of the M/N-major loader and fragment
+  // reader let the transposing reads run while those loads are in flight).
+  // Measured exception: the three-stage 256 x 128 tile with M/N-major
+  // operands runs faster with the loads in its last sub-step (its deeper
+  // pipeline already hides the latency, and the early loads contend with
+  // the transposing reads).
+  static constexpr bool kLateMN = !(C::AKC && C::BKC) && C::NSTAGE == 3;
+  typedef std::conditional_t<kLateMN, SlabPlan<DA::INSTR, KK - 1, DB::INSTR, KK - 1>,
+                             SlabPlan<DA::INSTR, 0, DB::INSTR, 1>> Plan;
   constexpr int NS = C::NSTAGE;
 
   // The slabs of all accumulators form one sequence (operand pair 0's KT
