@@ -656,58 +656,58 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
                              SlabPlan<DA::INSTR, 0, DB::INSTR, 1>> Plan;
   constexpr int NS = C::NSTAGE;
 
-  // The slabs of all accumulators form one sequence (operand pair 0's KT
+  // The slabs of all accumulators form one sequence (operand pair 0's
   // slabs, then pair 1's, ...) streamed through one pipeline, so the loads
-  // of the next pair overlap the last steps of the current one. The cursor
-  // (iq, ik) names the next slab to issue; past the end of the sequence the
-  // loads are issued out of range and fetch nothing. Every step issues
-  // exactly one slab, so L * (NS-2) loads still outstanding means the slab
-  // to be read has landed.
-  int iq = 0, ik = 0;
-  auto issue_slab = [&](char* st, auto a_tag, auto b_tag) {
-    const bool live = iq < C::NACC && ik < KT;
-    const int q = live ? iq : 0;
+  // of the next pair overlap the last steps of the current one. Each pair
+  // takes KTe = max(KT, NS-1) steps (steps past KT read zeros), so the NS-1
+  // slabs in flight always belong to the current pair or the next one: the
+  // K loop of pair p runs in two parts, the second of which issues the first
+  // slabs of pair p+1. The pair of every load is thus a compile-time
+  // constant (no runtime operand selection in the loop). Past the last pair
+  // the loads are still issued, out of range (they fetch nothing), so every
+  // step issues exactly one slab and L * (NS-2) loads still outstanding
+  // means the slab to be read has landed.
+  const int KTe = KT > NS - 1 ? KT : NS - 1;
+  auto issue = [&](auto q_tag, int k, char* st, auto a_tag, auto b_tag) {
+    constexpr int Q = decltype(q_tag)::value < C::NACC ? decltype(q_tag)::value : 0;
+    constexpr bool past = decltype(q_tag)::value >= C::NACC;
+    const bool live = !past && k < KT;
     const uint32_t oob = live ? 0u : 0x80000000u;
-    const int k0 = kbeg + ik * C::BK;
-    __amdgpu_buffer_rsrc_t rsa = ra[0], rsb = rb[0];
-    int64_t la = lda_b[0], lb = ldb_b[0];
-    static_for<1, C::NACC>([&](auto p) {
-      if (q == p) { rsa = ra[p]; rsb = rb[p]; la = lda_b[p]; lb = ldb_b[p]; }
-    });
-    if constexpr (decltype(a_tag)::value) DA::issue(rsa, la, k0, st, wave, lane, oob);
-    if constexpr (decltype(b_tag)::value) DB::issue(rsb, lb, k0, st + C::A_BYTES, wave, lane, oob);
-  };
-  auto advance = [&]() {
-    if (++ik >= KT) { ik = 0; ++iq; }
+    const int k0 = kbeg + (live ? k : 0) * C::BK;
+    if constexpr (decltype(a_tag)::value) DA::issue(ra[Q], lda_b[Q], k0, st, wave, lane, oob);
+    if constexpr (decltype(b_tag)::value) DB::issue(rb[Q], ldb_b[Q], k0, st + C::A_BYTES, wave, lane, oob);
   };
   static_for<0, NS - 1>([&](auto s) {
-    issue_slab(smem + s() * C::STAGE_BYTES, std::true_type{}, std::true_type{});
-    advance();
+    issue(std::integral_constant<int, 0>{}, s(), smem + s() * C::STAGE_BYTES, std::true_type{}, std::true_type{});
   });
   int cur = 0;       // stage read in this step
   int nxt = NS - 1;  // stage refilled in this step
+  // One K step on pair p whose loads fetch slab k of pair Q.
+  auto step = [&](auto p, auto q_tag, int k) {
+    // Slabs of the next NS-1 steps are in flight; wait for this one only.
+    wait_vmcnt<L * (NS - 2)>();
+    // A plain s_barrier: __syncthreads() would add a release fence that
+    // waits for every outstanding load, including the slabs still allowed
+    // in flight. The empty asm statements keep the compiler from moving
+    // LDS accesses across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // The slab NS-1 steps ahead goes to the stage last read in the
+    // previous step, which every wave has finished once past the barrier.
+    char* st = smem + nxt * C::STAGE_BYTES;
+    const char* As = smem + cur * C::STAGE_BYTES;
+    compute(p, As, As + C::A_BYTES, Plan{}, [&](auto kk) {
+      issue(q_tag, k, st, std::bool_constant<kk == Plan::A_AT>{}, std::bool_constant<kk == Plan::B_AT>{});
+    });
+    cur = cur + 1 == NS ? 0 : cur + 1;
+    nxt = nxt + 1 == NS ? 0 : nxt + 1;
+  };
   static_for<0, C::NACC>([&](auto p) {
-    for (int kt = 0; kt < KT; ++kt) {
-      // Slabs of the next NS-1 steps are in flight; wait for this one only.
-      wait_vmcnt<L * (NS - 2)>();
-      // A plain s_barrier: __syncthreads() would add a release fence that
-      // waits for every outstanding load, including the slabs still allowed
-      // in flight. The empty asm statements keep the compiler from moving
-      // LDS accesses across the barrier.
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      // The slab NS-1 steps ahead goes to the stage last read in the
-      // previous step, which every wave has finished once past the barrier.
-      char* st = smem + nxt * C::STAGE_BYTES;
-      const char* As = smem + cur * C::STAGE_BYTES;
-      compute(p, As, As + C::A_BYTES, Plan{}, [&](auto kk) {
-        issue_slab(st, std::bool_constant<kk == Plan::A_AT>{}, std::bool_constant<kk == Plan::B_AT>{});
-      });
-      advance();
-      cur = cur + 1 == NS ? 0 : cur + 1;
-      nxt = nxt + 1 == NS ? 0 : nxt + 1;
-    }
+    constexpr int P = decltype(p)::value;
+    for (int kt = 0; kt < KTe - (NS - 1); ++kt) step(p, std::integral_constant<int, P>{}, kt + NS - 1);
+    for (int kt = KTe - (NS - 1); kt < KTe; ++kt)
+      step(p, std::integral_constant<int, P + 1>{}, kt + NS - 1 - KTe);
   });
   // Out-of-range loads still count; none may land after the epilogue
   // starts reusing this LDS.
