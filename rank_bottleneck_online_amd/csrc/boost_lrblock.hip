@@ -696,7 +696,7 @@ int lrmlp_check_desc(const boost_lrmlp_desc* d) {
 struct LrmlpPlan {
   Choice down1, dual, down2, up2;                       // forward
   Choice ds2, dB2, rec, dA2, ds1, dB1, dA1, dx1;        // backward
-  size_t f_A1T, f_B1T, f_A2T, f_B2T, f_S1, f_M, f_S2, f_part, fwd_bytes;
+  size_t f_A1T, f_B2T, f_S1, f_M, f_S2, f_part, fwd_bytes;
   size_t b_B1T, b_S2, b_dU2, b_S1, b_M, b_dY, b_dU1, b_q, b_dg, b_part, bwd_bytes;
   size_t fwd_largest, bwd_largest;
 };
@@ -719,8 +719,6 @@ LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
   p.dx1 = choose(dt, T, D, 2 * r, 1, false, false);
   WsLayout f;
   p.f_A1T = f.take((size_t)(D * 2 * r * es));
-  p.f_B1T = f.take((size_t)(2 * r * F * es));
-  p.f_A2T = f.take((size_t)(F * r * es));
   p.f_B2T = f.take((size_t)(r * D * es));
   p.f_S1 = f.take((size_t)(T * 2 * r * es));
   p.f_M = f.take((size_t)(T * F * es));
@@ -1020,20 +1018,19 @@ int boost_lrmlp_fwd_chained(const boost_lrmlp_desc* d, const void* x, const void
   RBO_TRY(check_ws(ws, ws_bytes, p.fwd_bytes));
   hipStream_t s = as_stream(stream);
   void* A1T = at(ws, p.f_A1T);
-  void* B1T = at(ws, p.f_B1T);
-  void* A2T = at(ws, p.f_A2T);
   void* B2T = at(ws, p.f_B2T);
   void* S1 = at(ws, p.f_S1);
   void* M = at(ws, p.f_M);
   void* S2 = at(ws, p.f_S2);
   const float inv = 1.f / (float)D;
-  // K-contiguous weight operands (gain folded into the first down weights).
-  RBO_TRY(launch_transposes(dt,
-                            {{A1_cat, g, A1T, D, 2 * r, 1},
-                             {B1, nullptr, B1T, r, F, 2},
-                             {A2, nullptr, A2T, F, r, 1},
-                             {B2, nullptr, B2T, r, D, 1}},
-                            s));
+  // K-contiguous copies of the first down weights (with the gain folded
+  // in) and of the last up weights. B1 and A2 are read as they are stored,
+  // N-contiguous: for those two products the M/N-major operand path costs
+  // less than the transposes it avoids (measured at the 7B MLP shape: each
+  // within 2% of its K-contiguous time, against about 50 us of transposes
+  // saved), while the first down and last up products run 24% and 26%
+  // slower M/N-major, more than their transposes cost.
+  RBO_TRY(launch_transposes(dt, {{A1_cat, g, A1T, D, 2 * r, 1}, {B2, nullptr, B2T, r, D, 1}}, s));
   {  // H1 = rho * (x @ (g * A1_cat)), S1 = act(H1), sumsq
     GemmOps ops{};
     ops.a[0] = opnd(x, D, T, D, es);
@@ -1050,17 +1047,17 @@ int boost_lrmlp_fwd_chained(const boost_lrmlp_desc* d, const void* x, const void
     GemmOps ops{};
     ops.a[0] = opnd(S1, 2 * r, T, r, es);
     ops.a[1] = opnd(static_cast<const char*>(S1) + r * es, 2 * r, T, r, es);
-    ops.b[0] = opnd(B1T, r, F, r, es);
-    ops.b[1] = opnd(static_cast<const char*>(B1T) + F * r * es, r, F, r, es);
+    ops.b[0] = opnd(B1, F, r, F, es);
+    ops.b[1] = opnd(static_cast<const char*>(B1) + r * F * es, F, r, F, es);
     EpiSwiglu::Args ea{M, F};
-    RBO_TRY((gemm<EpiSwiglu, true, true, 2>("mlp_up1_swiglu", dt, p.dual, T, F, r, 1, ops, ea, s)));
+    RBO_TRY((gemm<EpiSwiglu, true, false, 2>("mlp_up1_swiglu", dt, p.dual, T, F, r, 1, ops, ea, s)));
   }
   {  // H2 = M @ A2, S2 = act(H2)
     GemmOps ops{};
     ops.a[0] = opnd(M, F, T, F, es);
-    ops.b[0] = opnd(A2T, F, r, F, es);
+    ops.b[0] = opnd(A2, r, F, r, es);
     EpiDown<false>::Args ea{H2, S2, nullptr, r, 0.f, 0.f, d->act, nullptr};
-    RBO_TRY((gemm<EpiDown<false>, true, true, 1>("mlp_down2", dt, p.down2, T, r, F, 1, ops, ea, s)));
+    RBO_TRY((gemm<EpiDown<false>, true, false, 1>("mlp_down2", dt, p.down2, T, r, F, 1, ops, ea, s)));
   }
   {  // Y = S2 @ B2
     GemmOps ops{};
@@ -1150,6 +1147,11 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void
   }
   // S1 = act(H1) recomputed from the saved bottleneck.
   RBO_TRY(launch_act_quant(dt, H1, S1, T * 2 * r, d->act, s));
+  // The three products of the recompute share one operand layout, K
+  // contiguous: A2 already is, B1 gets a transposed copy (measured: with
+  // all three M/N-major instead, B1 read as stored and A2 copied, the
+  // recompute at the 7B MLP shape ran 15% slower, 100 us, against 17 us
+  // of transpose saved).
   void* B1T = at(ws, p.b_B1T);
   RBO_TRY(launch_transposes(dt, {{B1, nullptr, B1T, r, F, 2}}, s));
   {  // recompute Yg, Yu and dM = dU2 @ A2^T in the same tile; M, dYg, dYu
