@@ -36,7 +36,9 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "low-rank block fwd+bwd TFLOP/s (% bf16 MFMA peak) + tokens/s, 7B shape"
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_json_path(workload: str) -> str:
+    """Counter-measured traffic of a workload's launches (written by --traffic)."""
+    return os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
 
 
 def log(*a):
@@ -477,6 +479,35 @@ MLP_LABEL_PATTERNS = {
 }
 
 
+# The forward of a grouped block (the QKV workload): down product with the
+# statistic and activation, batched up product with a plain store.
+LRBLOCK_FWD_LABEL_PATTERNS = {
+    "lrblock_down": "NS_7EpiDownILb1",
+    "lrblock_up": "NS_8EpiStoreILb0",
+}
+
+
+def lrblock_fwd_kernel_rw(T, d, r, G, d_out):
+    """(read, written) algorithmic bytes of the grouped block's forward
+    launches (bf16 operands, fp32 H and statistic)."""
+    b, f = 2, 4
+    return {"lrblock_down": (T * d * b + d * G * r * b, T * G * r * (f + b) + T * f),
+            "lrblock_up": (T * G * r * b + G * r * d_out * b, G * T * d_out * b)}
+
+
+def counter_workload(workload: str):
+    """(label patterns, {label: flops}, {label: (read, written)}) of a
+    workload whose launches the counter summaries cover."""
+    w = synth.WORKLOADS[workload]
+    if w["kind"] == "lrmlp":
+        a = {k: w[k] for k in ("T", "d", "r", "ffn")}
+        return MLP_LABEL_PATTERNS, mlp_kernel_flops(**a), mlp_kernel_rw(**a)
+    if w["kind"] == "lrblock" and workload.endswith("_fwd"):
+        return (LRBLOCK_FWD_LABEL_PATTERNS, lrblock_kernel_flops(w["T"], w["d"], w["r"], w["G"], w["d_out"], False),
+                lrblock_fwd_kernel_rw(w["T"], w["d"], w["r"], w["G"], w["d_out"]))
+    raise SystemExit(f"counter summaries cover the 7B MLP and the QKV forward, not {workload}")
+
+
 def short_kernel_name(n: str) -> str:
     import re
     m = re.search(r"CfgI(DF16b|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELb(\d)ELb(\d)ELi(\d)EEENS_(\d+)", n)
@@ -518,17 +549,17 @@ def counter_per_kernel(csv_path: str, counter: str):
     return per
 
 
-def mfma_summary(csv_path: str, title: str, command: str) -> str:
+def mfma_summary(csv_path: str, title: str, command: str, workload: str = "llama2_7b_mlp") -> str:
     """Markdown table of MFMA utilisation (rocprofv3 derived counter MfmaUtil)
     and hardware-counted bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
-    per labelled kernel of the MLP step, against its algorithmic flops."""
+    per labelled kernel of the workload's step, against its algorithmic flops."""
     util = counter_per_kernel(csv_path, "MfmaUtil")
     mops = counter_per_kernel(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
-    kf = mlp_kernel_flops(**{k: synth.WORKLOADS["llama2_7b_mlp"][k] for k in ("T", "d", "r", "ffn")})
+    patterns, kf, _ = counter_workload(workload)
     out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
            "| launch | kernel | MFMA busy (% of SIMD cycles) | counted MFMA GF | algorithmic GF | counted / algorithmic |",
            "|---|---|---|---|---|---|"]
-    for label, pat in MLP_LABEL_PATTERNS.items():
+    for label, pat in patterns.items():
         un = [k for k in util if pat in k]
         mn = [k for k in mops if pat in k]
         if len(un) != 1 or len(mn) != 1:
@@ -557,7 +588,8 @@ def traffic_json(fetch_csv: str, write_csv: str, workload: str, copy_mib: int) -
         raise SystemExit("no calibration copy kernel in the counter files")
     f_scale, w_scale = known / (fk * 1024.0), known / (wk * 1024.0)
     kernels = {}
-    for label, pat in MLP_LABEL_PATTERNS.items():
+    patterns = counter_workload(workload)[0]
+    for label, pat in patterns.items():
         fn = [k for k in fetch if pat in k]
         wn = [k for k in write if pat in k]
         if len(fn) != 1 or len(wn) != 1:
@@ -575,8 +607,7 @@ def traffic_table(json_path: str, title: str, command: str) -> str:
     """Markdown table of the per-launch traffic in a traffic JSON against the
     algorithmic bytes of each launch."""
     tj = json.load(open(json_path))
-    w = synth.WORKLOADS[tj["workload"]]
-    rw = mlp_kernel_rw(w["T"], w["d"], w["r"], w["ffn"])
+    rw = counter_workload(tj["workload"])[2]
     cal = tj["calibration"]
     out = [f"# {title}", "", "Commands (R = repository root):", "", "```", command, "```", "",
            f"Calibration: each run first copies {cal['copy_bytes'] >> 20} MiB with one blit kernel. FETCH_SIZE read "
@@ -586,7 +617,8 @@ def traffic_table(json_path: str, title: str, command: str) -> str:
            "last-level (MALL) cache count too: fetched bytes are upper bounds on DRAM bytes.", "",
            f"Source digest of the kernels measured: `{tj['source_digest']}`.", "",
            "Algorithmic bytes: each input read once, each output written once (the operands of every launch are "
-           "listed in `mlp_kernel_rw` in bench.py). Fetched bytes above the algorithmic reads are operand panels "
+           "listed in `mlp_kernel_rw` / `lrblock_fwd_kernel_rw` in bench.py). Fetched bytes above the algorithmic "
+           "reads are operand panels "
            "that many tiles share and that leave an XCD's 4 MB L2 between the waves of tiles using them (the "
            "up projections and the recompute, with K = r, re-read their S1/B1 panels once per wave of tiles); "
            "they are served from the fabric (MALL or DRAM).", "",
@@ -627,6 +659,10 @@ def r_sweep(B, torch, ranks, steps, warmup):
 
 # ---------------------------------------------------------------------------
 
+def peak_of(wl) -> float:
+    return PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -659,6 +695,10 @@ def main():
                     "line of per-launch kernel times (ms, library events, mean of --steps steps) per rank, and exit. "
                     "The K = r products have a fixed tile count, so their time against r separates the fixed "
                     "per-tile cost from the main loop")
+    ap.add_argument("--isolate-steps", type=int, default=3,
+                    help="after the timed steps, run this many more (not part of `value`) with every product "
+                         "on the caller's stream, one launch at a time, and report each product's own time "
+                         "as `kernels_isolated` (0: skip)")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
@@ -666,7 +706,7 @@ def main():
         sys.stdout.write(summarize_stats(args.summarize_stats, args.title, args.command))
         return
     if args.mfma_summary:
-        sys.stdout.write(mfma_summary(args.mfma_summary, args.title, args.command))
+        sys.stdout.write(mfma_summary(args.mfma_summary, args.title, args.command, args.workload))
         return
     if args.traffic_table:
         sys.stdout.write(traffic_table(args.traffic_table, args.title, args.command))
@@ -768,6 +808,31 @@ def main():
                    "tflops_median": round(wl.flops / (fms[len(fms) // 2] * 1e-3) / 1e12, 2)}
         del scratch
 
+    # Third pass, not part of `value`: every product alone. The weight
+    # gradients leave the side stream for the caller's (the library's
+    # measurement switch), so no launch shares the GPU with another and each
+    # product's time is its own (the cache state is still that of a step).
+    isolated = None
+    if args.isolate_steps > 0:
+        B.profiler_serialize(True)
+        B.profiler_enable(None, 4096)
+        for _ in range(args.isolate_steps):
+            wl.step()
+        torch.cuda.synchronize()
+        rep_iso = B.profiler_report()
+        B.profiler_disable()
+        B.profiler_serialize(False)
+        isolated = {}
+        for k, (c, t) in sorted(rep_iso.items(), key=lambda kv: -kv[1][1]):
+            kms = t / args.isolate_steps
+            isolated[k] = {"ms": round(kms, 4), "launches_per_step": c / args.isolate_steps}
+            kf = wl.kflops.get(k)
+            if kf and kms > 0:
+                isolated[k]["tflops"] = round(kf / (kms * 1e-3) / 1e12, 1)
+                isolated[k]["frac"] = round(kf / (kms * 1e-3) / 1e12 / peak_of(wl), 4)
+        log("kernel times in one step, each product alone (ms):",
+            json.dumps({k: v["ms"] for k, v in isolated.items()}))
+
     # Optional: the same step captured into a HIP graph and replayed (the
     # library allocates nothing and forks its side stream with events, which
     # capture records as graph dependencies); launch-bound workloads show the
@@ -796,13 +861,13 @@ def main():
     launches_per_step = cnt / args.steps
     dom_flops = wl.kflops.get(dom)
     value = wl.flops / (ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = peak_of(wl)
     roofline = None
     if dom_flops:
         achieved = dom_flops / (avg_ms * 1e-3) / 1e12
         traffic = None
-        if os.path.exists(TRAFFIC_JSON):
-            tj = json.load(open(TRAFFIC_JSON))
+        if os.path.exists(traffic_json_path(args.workload)):
+            tj = json.load(open(traffic_json_path(args.workload)))
             if tj.get("source_digest") == source_digest() and tj.get("workload") == args.workload:
                 k = tj.get("kernels", {}).get(dom)
                 if k:
@@ -866,6 +931,7 @@ def main():
                    "model_only_gflop_per_step": round(wl.model_flops / 1e9, 2),
                    "mall_flushed": flushed, "graph": graph},
         "kernels": kernels,
+        "kernels_isolated": isolated,
     }
     print(json.dumps(out), flush=True)
 

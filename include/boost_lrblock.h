@@ -295,6 +295,16 @@ int boost_profiler_enable(const char* name_filter, int max_records);
 int boost_profiler_report(char* buf, size_t len);
 int boost_profiler_disable(void);
 
+/* Measurement switch, off by default (on = 1 sets it, 0 clears it; any
+ * other value is BOOST_ERR_INVALID_VALUE). While set, backward passes
+ * enqueue their weight-gradient products on the caller's stream instead of
+ * the side stream, so every launch runs with no other kernel of the call
+ * beside it and a timed launch measures that product alone. Results are
+ * bit-identical either way (the same kernels compute the same sums); only
+ * the overlap, and so the wall time of a backward, changes. Read when a
+ * backward call starts; process-global and not thread-safe, like the timer. */
+int boost_profiler_serialize(int on);
+
 #ifdef __cplusplus
 }
 #endif

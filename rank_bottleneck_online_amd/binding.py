@@ -74,6 +74,7 @@ _SIGS = {
     "boost_profiler_enable": ([ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
     "boost_profiler_report": ([ctypes.c_char_p, _SZ], ctypes.c_int),
     "boost_profiler_disable": ([], ctypes.c_int),
+    "boost_profiler_serialize": ([ctypes.c_int], ctypes.c_int),
 }
 
 _lib = None
@@ -616,3 +617,8 @@ def profiler_report() -> dict:
 
 def profiler_disable() -> None:
     _check(lib().boost_profiler_disable(), "boost_profiler_disable")
+
+
+def profiler_serialize(on: bool) -> None:
+    """Weight gradients on the caller's stream (True) or the side stream."""
+    _check(lib().boost_profiler_serialize(1 if on else 0), "boost_profiler_serialize")

@@ -63,6 +63,10 @@ struct Profiler {
   size_t used = 0;
 } g_prof;
 thread_local int t_prof_pending = -1;
+// Measurement switch: while set, backward passes enqueue their weight
+// gradients on the caller's stream (see SideFork), so every launch runs
+// alone and its timed duration is its own.
+bool g_serial_side = false;
 
 void prof_begin(const char* label, hipStream_t s) {
   t_prof_pending = -1;
@@ -470,9 +474,11 @@ int stream_after(hipStream_t to, hipStream_t from, Side* sd) {
 // keeps the first error). So whatever a backward returns, work it enqueued
 // on the side stream is ordered before later work on the caller's stream,
 // and a stream capture never ends with the side stream unjoined.
+// With the measurement switch g_serial_side set (read once, at
+// construction), side() is the caller's stream and fork/join do nothing.
 class SideFork {
  public:
-  SideFork(Side* sd, hipStream_t main) : sd_(sd), main_(main) {}
+  SideFork(Side* sd, hipStream_t main) : sd_(sd), main_(main), serial_(g_serial_side) {}
   ~SideFork() {
     if (forked_) {
       const std::string keep = g_detail;
@@ -482,9 +488,10 @@ class SideFork {
   }
   SideFork(const SideFork&) = delete;
   SideFork& operator=(const SideFork&) = delete;
-  hipStream_t side() const { return sd_->s; }
+  hipStream_t side() const { return serial_ ? main_ : sd_->s; }
   // The side stream waits for everything enqueued on the caller's so far.
   int fork() {
+    if (serial_) return BOOST_OK;
     RBO_TRY(stream_after(sd_->s, main_, sd_));
     forked_ = true;
     return BOOST_OK;
@@ -499,6 +506,7 @@ class SideFork {
  private:
   Side* sd_;
   hipStream_t main_;
+  bool serial_;
   bool forked_ = false;
 };
 
@@ -1357,6 +1365,13 @@ int boost_attn_standin_bwd(int dtype, int64_t T, int64_t d, const void* da, void
                        static_cast<float*>(dqkv), (int64_t)n);
   prof_end(s);
   return check_launch("attn_standin_bwd");
+}
+
+int boost_profiler_serialize(int on) {
+  g_detail.clear();
+  if (on != 0 && on != 1) return fail(BOOST_ERR_INVALID_VALUE, "on = %d must be 0 or 1", on);
+  g_serial_side = on != 0;
+  return BOOST_OK;
 }
 
 int boost_profiler_enable(const char* name_filter, int max_records) {

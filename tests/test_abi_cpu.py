@@ -53,6 +53,14 @@ def test_abi_version_and_status_strings(B):
     assert L.boost_status_string(99).decode() == "BOOST_ERR_UNKNOWN"
 
 
+def test_serialize_switch_validates_and_toggles(B):
+    L = B.lib()
+    assert L.boost_profiler_serialize(2) == 1
+    assert "must be 0 or 1" in L.boost_last_error_detail().decode()
+    assert L.boost_profiler_serialize(1) == 0
+    assert L.boost_profiler_serialize(0) == 0
+
+
 # Fake, 256-byte aligned, non-overlapping "device" addresses: validation only
 # compares them, it never dereferences them.
 class Fake:

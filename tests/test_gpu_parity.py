@@ -186,6 +186,27 @@ def test_bit_identical_reruns(B):
         assert torch.equal(a[k], b[k]), k
 
 
+def test_serialized_weight_gradients_bit_identical(B):
+    # The measurement switch moves the weight gradients of every backward to
+    # the caller's stream: same kernels, same sums, so every output matches
+    # the overlapped run bit for bit (MLP with split-K partials, block, share).
+    say("serialized weight gradients: lrmlp T=2500 (split-K), lrblock T=300, btp share T=300")
+    mlp = synth.lrmlp_inputs(2500, 128, 64, 192, dtype="bf16", seed=6)
+    blk = synth.lrblock_inputs(300, 256, 128, 3, 256, dtype="bf16", seed=6)
+    sh = synth.btp_shard(synth.btp_inputs(300, 192, 1280, 4, dtype="bf16", seed=6), 0, 4)
+    runs = []
+    for serial in (False, True):
+        B.profiler_serialize(serial)
+        try:
+            runs.append((run_lrmlp(B, mlp, "bf16", "silu"), run_lrblock(B, blk, "bf16", "silu", True),
+                         run_btp(B, sh, "bf16")))
+        finally:
+            B.profiler_serialize(False)
+    for a, b in zip(*runs):
+        for k in a:
+            assert torch.equal(a[k], b[k]), k
+
+
 def test_scale_invariance_with_zero_eps(B):
     # Online-RMSNorm with eps = 0: scaling x by 2^k (exact in bf16) leaves the
     # block's output unchanged and stays finite far from unit scale.
