@@ -203,6 +203,8 @@ class Workload:
             self.fwd, self.bwd_fn = fwd, (bwd if self.bwd else None)
             self.tokens = T
             self.kflops = lrblock_kernel_flops(T, d, r, G, n, self.bwd)
+            if not self.bwd:
+                self.kbytes = {k: rd + wr for k, (rd, wr) in lrblock_fwd_kernel_rw(T, d, r, G, n).items()}
             self.shape = dict(T=T, d=d, r=r, G=G, d_out=n)
         elif self.kind == "btp":
             T, r, D, P = w["T"], w["r"], w["d_global"], w["P"]
@@ -549,6 +551,19 @@ def counter_per_kernel(csv_path: str, counter: str):
     return per
 
 
+def dispatch_ns(csv_path: str, pattern: str):
+    """Durations (ns) of the dispatches whose kernel name contains pattern,
+    one per dispatch, from a counter_collection.csv."""
+    import csv
+    seen, out = set(), []
+    for r in csv.DictReader(open(csv_path)):
+        if pattern not in r["Kernel_Name"] or r["Dispatch_Id"] in seen:
+            continue
+        seen.add(r["Dispatch_Id"])
+        out.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
 def mfma_summary(csv_path: str, title: str, command: str, workload: str = "llama2_7b_mlp") -> str:
     """Markdown table of MFMA utilisation (rocprofv3 derived counter MfmaUtil)
     and hardware-counted bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
@@ -598,6 +613,9 @@ def traffic_json(fetch_csv: str, write_csv: str, workload: str, copy_mib: int) -
         kernels[label] = {"kernel": short_kernel_name(fn[0]), "dispatches": len(fv),
                           "fetch_bytes": round(sum(fv) / len(fv) * 1024.0 * f_scale),
                           "write_bytes": round(sum(wv) / len(wv) * 1024.0 * w_scale)}
+        durs = dispatch_ns(fetch_csv, pat) + dispatch_ns(write_csv, pat)
+        if durs:
+            kernels[label]["avg_ms_profiled"] = round(sum(durs) / len(durs) / 1e6, 5)
     return {"source_digest": source_digest(), "workload": workload,
             "calibration": {"copy_bytes": int(known), "fetch_kib_read": fk, "write_kib_read": wk,
                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
@@ -622,12 +640,22 @@ def traffic_table(json_path: str, title: str, command: str) -> str:
            "that many tiles share and that leave an XCD's 4 MB L2 between the waves of tiles using them (the "
            "up projections and the recompute, with K = r, re-read their S1/B1 panels once per wave of tiles); "
            "they are served from the fabric (MALL or DRAM).", "",
+           "Rates: the counted bytes (fetched + written) and the algorithmic bytes over each launch's average "
+           "duration in the two counter runs (kernels run one at a time under counter collection), against the "
+           f"{PEAK_HBM_GBS / 1e3:.0f} TB/s HBM peak.", "",
            "| launch | kernel | fetched MB | written MB | algorithmic read MB | algorithmic write MB | "
-           "fetched / algorithmic read |", "|---|---|---|---|---|---|---|"]
+           "fetched / algorithmic read | us (profiled) | counted GB/s | % of HBM peak | algorithmic GB/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
     for label, k in tj["kernels"].items():
         rd, wr = rw[label]
+        ms = k.get("avg_ms_profiled")
+        if ms:
+            cg = (k["fetch_bytes"] + k["write_bytes"]) / (ms * 1e-3) / 1e9
+            rates = f"{ms * 1e3:.1f} | {cg:.0f} | {100 * cg / PEAK_HBM_GBS:.1f} | {(rd + wr) / (ms * 1e-3) / 1e9:.0f}"
+        else:
+            rates = "- | - | - | -"
         out.append(f"| {label} | {k['kernel']} | {k['fetch_bytes'] / 1e6:.0f} | {k['write_bytes'] / 1e6:.0f} | "
-                   f"{rd / 1e6:.0f} | {wr / 1e6:.0f} | {k['fetch_bytes'] / rd:.2f} |")
+                   f"{rd / 1e6:.0f} | {wr / 1e6:.0f} | {k['fetch_bytes'] / rd:.2f} | {rates} |")
     return "\n".join(out) + "\n"
 
 def r_sweep(B, torch, ranks, steps, warmup):
