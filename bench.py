@@ -557,9 +557,9 @@ def dispatch_ns(csv_path: str, pattern: str):
     import csv
     seen, out = set(), []
     for r in csv.DictReader(open(csv_path)):
-        if pattern not in r["Kernel_Name"] or r["Dispatch_Id"] in seen:
+        if pattern not in r["Kernel_Name"] or not r.get("Start_Timestamp") or r.get("Dispatch_Id") in seen:
             continue
-        seen.add(r["Dispatch_Id"])
+        seen.add(r.get("Dispatch_Id"))
         out.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     return out
 

@@ -6,6 +6,7 @@ the kernel-name shortener used by the profile summaries, the calibration of
 the FETCH_SIZE / WRITE_SIZE counters, and the one-GPU guard.
 """
 import csv
+import json
 import os
 import subprocess
 import sys
@@ -94,6 +95,30 @@ def test_traffic_calibration(tmp_path):
     assert k["fetch_bytes"] == 2000 * 1024 * 2
     assert k["write_bytes"] == 500 * 1024
     assert tj["source_digest"] == bench.source_digest()
+
+
+def test_traffic_rates_from_dispatch_times(tmp_path):
+    # Two dispatches of 100 and 300 us in each counter run: the launch
+    # averages 200 us, and the table turns (fetched + written) bytes into
+    # GB/s against the HBM peak.
+    fetch, write = str(tmp_path / "f.csv"), str(tmp_path / "w.csv")
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    for path, cnt, cal in ((fetch, "FETCH_SIZE", 1048576.0), (write, "WRITE_SIZE", 1048576.0)):
+        with open(path, "w", newline="") as f:
+            wr = csv.DictWriter(f, fieldnames=cols)
+            wr.writeheader()
+            wr.writerow(dict(zip(cols, (1, "__amd_rocclr_copyBuffer", cnt, cal, 0, 10))))
+            wr.writerow(dict(zip(cols, (2, SWIGLU_BWD, cnt, 390625.0, 1000, 101000))))
+            wr.writerow(dict(zip(cols, (3, SWIGLU_BWD, cnt, 390625.0, 200000, 500000))))
+    tj = bench.traffic_json(fetch, write, "llama2_7b_mlp", 1024)
+    k = tj["kernels"]["mlp_recompute_swiglu_bwd"]
+    assert k["avg_ms_profiled"] == pytest.approx(0.2)
+    assert k["fetch_bytes"] == k["write_bytes"] == 400_000_000
+    jp = tmp_path / "t.json"
+    jp.write_text(json.dumps(tj))
+    row = [ln for ln in bench.traffic_table(str(jp), "t", "c").splitlines() if ln.startswith("| mlp_recompute")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[7] == "200.0" and cells[8] == "4000" and cells[9] == "50.0"
 
 
 def test_traffic_needs_the_calibration_copy(tmp_path):
