@@ -40,19 +40,20 @@
  *   - Ownership: the caller owns every buffer. The library allocates no
  *     device memory, frees nothing, keeps no pointer after return and never
  *     synchronises. Work is enqueued on `stream` (a hipStream_t; NULL = the
- *     default stream) in stream order and runs asynchronously. The backward
- *     calls fork their weight-gradient products onto a side stream through
- *     an event recorded on `stream`, and make `stream` wait for them before
- *     returning - on every return path, errors included, once anything was
- *     forked - so all results are ordered on `stream` exactly as if
- *     everything ran on it; stream capture of `stream` captures both.
+ *     default stream) in stream order and runs asynchronously. The block and
+ *     MLP backward calls fork their weight-gradient products onto a side
+ *     stream through an event recorded on `stream`, and make `stream` wait
+ *     for them before returning - on every return path, errors included,
+ *     once anything was forked - so all results are ordered on `stream`
+ *     exactly as if everything ran on it; stream capture of `stream`
+ *     captures both. The BTP share backward runs on `stream` alone.
  *   - State: besides the loaded kernels, the library keeps one side stream
  *     and four events per host thread and device, created on first use
  *     with the default priority and kept until the process ends (no device
- *     memory). Two backward calls made from one host thread on different
- *     streams share that thread's side stream, so their weight-gradient
- *     products run one after the other (results are unaffected; only the
- *     overlap between the two calls is lost).
+ *     memory). Two block or MLP backward calls made from one host thread
+ *     on different streams share that thread's side stream, so their
+ *     weight-gradient products run one after the other (results are
+ *     unaffected; only the overlap between the two calls is lost).
  *   - Outputs are overwritten, never accumulated into. Inputs must not
  *     overlap outputs or the workspace.
  *   - Workspace: `ws` is device scratch of at least the size returned by the
