@@ -85,12 +85,13 @@ void prof_end(hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Tile configurations
 // ---------------------------------------------------------------------------
-enum CfgId { CFG_256x256 = 0, CFG_256x128 = 1, CFG_128x128 = 2, CFG_F32 = 3, CFG_192x256 = 4 };
+enum CfgId { CFG_256x256 = 0, CFG_256x128 = 1, CFG_128x128 = 2, CFG_F32 = 3, CFG_192x256 = 4, CFG_256x192 = 5 };
 struct CfgInfo {
   int bm, bn;
   double eff;  // relative MFMA efficiency used by the planner
 };
-constexpr CfgInfo kCfg[] = {{256, 256, 1.00}, {256, 128, 0.88}, {128, 128, 0.70}, {64, 64, 1.0}, {192, 256, 0.95}};
+constexpr CfgInfo kCfg[] = {{256, 256, 1.00}, {256, 128, 0.88}, {128, 128, 0.70}, {64, 64, 1.0}, {192, 256, 0.95},
+                            {256, 192, 0.95}};
 
 // bf16 tiles run 8 waves (two per SIMD): while one wave waits on a barrier,
 // an LDS read or a load issue, the other keeps the matrix core busy.
@@ -101,6 +102,11 @@ template <bool AKC, bool BKC, int NACC> using C128 = Cfg<bf16, 128, 128, 2, 4, A
 // fill well under the 256 CUs in one round (8192 x 1280 outputs: 160 tiles
 // of 256 x 256, 215 of 192 x 256). K-contiguous operands only.
 template <bool AKC, bool BKC, int NACC> using C192 = Cfg<bf16, 192, 256, 2, 4, AKC, BKC, NACC>;
+// 256 x 192 (64 x 96 wave tiles): N a multiple of 192 where 256 x 256 tiles
+// would leave half a round (the grouped QKV down products: 512 tiles in two
+// rounds against 768 of 256 x 128 in three). K-contiguous operands and
+// epilogues without row or column sums only (96 columns are 12 lanes).
+template <bool AKC, bool BKC, int NACC> using C256N192 = Cfg<bf16, 256, 192, 4, 2, AKC, BKC, NACC>;
 template <bool AKC, bool BKC, int NACC> using CF32 = Cfg<float, 64, 64, 2, 2, AKC, BKC, NACC>;
 
 struct Choice {
@@ -123,17 +129,18 @@ int krot_rule(CfgId, int64_t k_split) { return k_split >= 4096 ? 2 : 0; }
 // reduction can sum, the number of K splits) minimising a simple model:
 // full waves of 256 workgroups, each tile costing 2*BM*BN*Ksplit flops at a
 // shape-dependent efficiency, plus the HBM traffic of split partials. kc:
-// both operands are K-contiguous (the 192 x 256 tile is built for those).
+// both operands are K-contiguous (the 192 x 256 tile is built for those);
+// narrow: also an epilogue without row or column sums (the 256 x 192 tile).
 Choice choose(int dtype, int64_t M, int64_t N, int64_t K, int64_t batch, bool allow_split, bool dual,
-              bool kc = false) {
+              bool kc = false, bool narrow = false) {
   Choice best{};
   double best_t = 1e300;
   const int bk = dtype == BOOST_DT_F32 ? 32 : 64;
-  const CfgId ids_bf16[] = {CFG_256x256, CFG_256x128, CFG_128x128, CFG_192x256};
+  const CfgId ids_bf16[] = {CFG_256x256, CFG_256x128, CFG_128x128, CFG_192x256, CFG_256x192};
   const CfgId ids_dual[] = {CFG_256x128};
   const CfgId ids_f32[] = {CFG_F32};
   const CfgId* ids = dtype == BOOST_DT_F32 ? ids_f32 : (dual ? ids_dual : ids_bf16);
-  const int nids = dtype == BOOST_DT_F32 ? 1 : (dual ? 1 : (kc ? 4 : 3));
+  const int nids = dtype == BOOST_DT_F32 ? 1 : (dual ? 1 : (kc ? (narrow ? 5 : 4) : 3));
   const int split_opts[] = {1, 2, 4, 8};
   for (int ii = 0; ii < nids; ++ii) {
     const CfgInfo& ci = kCfg[ids[ii]];
@@ -205,6 +212,13 @@ int gemm(const char* label, int dtype, const Choice& ch, int64_t M, int64_t N, i
           return launch_cfg<C192<AKC, BKC, NACC>, E, TAG>(label, ch, m, n, k, b, ops, ea, s);
         } else {
           return fail(BOOST_ERR_UNSUPPORTED, "%s: 192 x 256 tiles need K-contiguous operands", label);
+        }
+      case CFG_256x192:
+        if constexpr (AKC && BKC && !E::kRowSum && !E::kColSum) {
+          return launch_cfg<C256N192<AKC, BKC, NACC>, E, TAG>(label, ch, m, n, k, b, ops, ea, s);
+        } else {
+          return fail(BOOST_ERR_UNSUPPORTED, "%s: 256 x 192 tiles need K-contiguous operands and no row sums",
+                      label);
         }
       default: return launch_cfg<C128<AKC, BKC, NACC>, E, TAG>(label, ch, m, n, k, b, ops, ea, s);
     }
@@ -554,7 +568,7 @@ LrblockPlan lrblock_plan(const boost_lrblock_desc* d) {
   LrblockPlan p{};
   const int dt = d->dtype;
   const int64_t T = d->T, D = d->d, r = d->r, G = d->G, n = d->d_out, es = esize(dt);
-  p.down = choose(dt, T, G * r, D, 1, false, false, true);
+  p.down = choose(dt, T, G * r, D, 1, false, false, true, true);
   p.up = choose(dt, T, n, r, G, false, false, true);
   p.ds = choose(dt, T, r, n, G, false, false, true);
   p.dB = choose(dt, r, n, T, G, true, false);
@@ -725,7 +739,7 @@ LrmlpPlan lrmlp_plan(const boost_lrmlp_desc* d) {
   LrmlpPlan p{};
   const int dt = d->dtype;
   const int64_t T = d->T, D = d->d, r = d->r, F = d->ffn, es = esize(dt);
-  p.down1 = choose(dt, T, 2 * r, D, 1, false, false, true);
+  p.down1 = choose(dt, T, 2 * r, D, 1, false, false, true, true);
   p.dual = choose(dt, T, F, r, 1, false, true);
   p.down2 = choose(dt, T, r, F, 1, false, false);
   p.up2 = choose(dt, T, D, r, 1, false, false, true);
@@ -795,11 +809,11 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   const int dt = d->dtype;
   const int64_t T = d->T, r = d->r, S = d->d_shard, es = esize(dt);
   p.u = choose(dt, T, S, r, 1, false, false, true);
-  p.p = choose(dt, T, r, S, 1, false, false, true);
+  p.p = choose(dt, T, r, S, 1, false, false, true, true);
   p.ue = choose(dt, T, S, r, 1, false, true);
   p.dA = choose(dt, S, r, T, 1, true, false);
   p.dB = choose(dt, r, S, T, 1, true, false);
-  p.dz = choose(dt, T, r, S, 1, false, false, true);
+  p.dz = choose(dt, T, r, S, 1, false, false, true, true);
   WsLayout f;
   p.f_BT = f.take((size_t)(r * S * es));
   p.f_AT = f.take((size_t)(S * r * es));

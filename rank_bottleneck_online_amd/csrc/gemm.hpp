@@ -418,8 +418,14 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
   constexpr int ER = C::EPI_ROWS, ROUNDS = 32 / ER;
   constexpr int V8 = C::WTN / 8;        // lanes per row in the read-back
   constexpr int RPS = 64 / V8;          // rows per read-back step
-  constexpr int STEPS = ER / RPS;       // read-back steps per staging round
-  static_assert(64 % V8 == 0 && ER % RPS == 0, "wave tile width must be 32, 64 or 128");
+  constexpr int STEPS = (ER + RPS - 1) / RPS;  // read-back steps per staging round
+  // With a wave tile 32, 64 or 128 wide every lane reads back a row in
+  // every step. With 96 (12 lanes per row, 5 rows per step) lanes 60-63
+  // idle and the last step's rows past the round are skipped; the row and
+  // column sums use lane butterflies, so reducing epilogues need the former.
+  constexpr bool kFull = 64 % V8 == 0 && ER % RPS == 0;
+  static_assert(kFull || !(E::kRowSum || E::kColSum), "row/column sums need a wave tile 32, 64 or 128 wide");
+  static_assert(V8 <= 64 && C::WTN % 8 == 0, "wave tile width");
   float* scr = reinterpret_cast<float*>(c.smem) + c.wave * (C::NACC * SUB);
   const int c8 = c.lane % V8, rsub = c.lane / V8;
 
@@ -436,8 +442,9 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
       // overlaps the staging, the barrier and each other.
       typename E::Pre pf[STEPS];
       static_for<0, STEPS>([&](auto s) {
-        E::template pre<C>(c, ea, c.wm * C::WTM + i * 32 + h * ER + s * RPS + rsub, c.wn * C::WTN + c8 * 8,
-                           pf[s]);
+        if (kFull || (rsub < RPS && s * RPS + rsub < ER))
+          E::template pre<C>(c, ea, c.wm * C::WTM + i * 32 + h * ER + s * RPS + rsub, c.wn * C::WTN + c8 * 8,
+                             pf[s]);
       });
       // MFMA register v holds row 8 (v/4) + 4 (lane/32) + v%4 of the block;
       // registers [16h/ROUNDS, 16(h+1)/ROUNDS) cover rows [h ER, (h+1) ER).
@@ -461,6 +468,7 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[C::NACC][C::FM][C::FN],
       asm volatile("" ::: "memory");
       static_for<0, STEPS>([&](auto s) {
         const int r = s * RPS + rsub;
+        if (!kFull && (rsub >= RPS || r >= ER)) return;
         const int lr = c.wm * C::WTM + i * 32 + h * ER + r;
         const int lc = c.wn * C::WTN + c8 * 8;
         float vals[C::NACC][8];

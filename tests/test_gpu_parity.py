@@ -78,6 +78,18 @@ def test_lrblock_global_width_divisor(B):
     compare_lrblock(out, inp, "bf16", "silu", True, d_norm=1024)
 
 
+def test_lrblock_parity_256x192_tiles(B):
+    # T = 4090, G r = 3072: 256 x 192 down tiles fill one round (16 x 16),
+    # where 192 x 256 needs two (22 x 12) and 256 x 256 leaves a quarter of
+    # the round idle, so the planner takes the 96-wide wave tiles whose
+    # epilogue reads back 12 lanes per row; ragged T.
+    T, d, r, G, n = 4090, 256, 1024, 3, 256
+    say(f"lrblock 256x192 down tiles T={T} d={d} r={r} G={G} n={n} bf16 silu seed=4")
+    inp = synth.lrblock_inputs(T, d, r, G, n, dtype="bf16", seed=4)
+    out = run_lrblock(B, inp, "bf16", "silu", True)
+    compare_lrblock(out, inp, "bf16", "silu", True)
+
+
 def run_lrmlp(B, inp, dtype, act, eps=1e-5):
     t = {k: dev(inp[k], dtype) for k in ("x", "g", "A1_cat", "B1", "A2", "B2", "dY")}
     Y, H1, H2, sumsq = B.lrmlp_fwd(t["x"], t["g"], t["A1_cat"], t["B1"], t["A2"], t["B2"], act=act, eps=eps)
