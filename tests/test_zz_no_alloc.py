@@ -82,14 +82,14 @@ def test_full_size_1b_qkv_forward_and_the_limit(B):
     check("Y rows", host(got[0])[:, rows], ref["Y"], "bf16")
     check("H rows", host(got[1])[rows], ref["H"], "bf16")
     # a forward whose scratch exceeds the fixed array is refused, nothing launched
-    x = torch.zeros((T, 4096), dtype=torch.bfloat16, device="cuda")
-    g = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
-    A = torch.zeros((4096, G * r), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((T, 8192), dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(8192, dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((8192, G * r), dtype=torch.bfloat16, device="cuda")
     Bw = torch.zeros((G, r, n), dtype=torch.bfloat16, device="cuda")
     out = (torch.zeros((G, T, n), dtype=torch.bfloat16, device="cuda"),
            torch.zeros((T, G * r), dtype=torch.float32, device="cuda"),
            torch.zeros(T, dtype=torch.float32, device="cuda"))
-    big = B.lrblock_desc(T, 4096, r, G, n, B.DT_BF16)
+    big = B.lrblock_desc(T, 8192, r, G, n, B.DT_BF16)
     assert B.lrblock_workspace_size(big, False) > 64 << 20
     with pytest.raises(B.BoostError, match="UNSUPPORTED"):
         B.lrblock_fwd_noalloc(x, g, A, Bw, out=out)
