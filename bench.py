@@ -86,8 +86,7 @@ def mlp_kernel_rw(T, d, r, ffn):
         "mlp_up1_swiglu": (T * 2 * r * b + 2 * r * ffn * b, T * ffn * b),
         "mlp_down2": (T * ffn * b + ffn * r * b, T * r * (f + b)),
         "mlp_up2": (T * r * b + r * d * b, T * d * b),
-        # also S1 = act(H1) for the recompute that follows (H1 read, S1 written)
-        "mlp_ds2": (T * d * b + r * d * b + T * r * f + T * 2 * r * f, 2 * T * r * b + T * 2 * r * b),
+        "mlp_ds2": (T * d * b + r * d * b + T * r * f, 2 * T * r * b),
         "mlp_dB2": (T * r * b + T * d * b, r * d * f),
         "mlp_recompute_swiglu_bwd": (T * 2 * r * b + 2 * r * ffn * b + T * r * b + ffn * r * b, 3 * T * ffn * b),
         "mlp_dA2": (T * ffn * b + T * r * b, ffn * r * f),

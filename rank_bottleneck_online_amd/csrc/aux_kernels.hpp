@@ -1,6 +1,7 @@
 // Small memory-bound kernels around the GEMMs: transposing weights into the
 // K-contiguous operand layout (folding the RMSNorm gain into the down
-// weights on the way) and the fixed-order reductions of per-tile partials.
+// weights on the way), recomputing the bottleneck activation from the saved
+// fp32 H, and the fixed-order reductions of per-tile partials.
 #pragma once
 
 #include "gemm.hpp"
@@ -142,6 +143,34 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposeJobs jobs)
       o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
       *reinterpret_cast<u32x4*>(dst + (int64_t)(tc + oc) * J.R + col) = o;
     }
+  }
+}
+
+// S = act(H) in the storage dtype (bottleneck activation recompute).
+template <typename T>
+__global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict__ H, T* __restrict__ S,
+                                                        int64_t n, int act) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    Elem<T>::store(S, i, act_f(H[i], act));
+}
+
+__global__ __launch_bounds__(256) void act_quant_bf16x8_kernel(const float4* __restrict__ H,
+                                                               u32x4* __restrict__ S, int64_t n8,
+                                                               int act) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 a = H[2 * i], b = H[2 * i + 1];
+    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      bf16x2 p;
+      p[0] = static_cast<bf16>(act_f(f[2 * w], act));
+      p[1] = static_cast<bf16>(act_f(f[2 * w + 1], act));
+      o[w] = __builtin_bit_cast(uint32_t, p);
+    }
+    S[i] = o;
   }
 }
 

@@ -290,6 +290,18 @@ int launch_transposes(int dtype, std::initializer_list<TJob> list, hipStream_t s
   return check_launch("weight_transpose");
 }
 
+int launch_act_quant(int dtype, const float* H, void* S, int64_t n, int act, hipStream_t s) {
+  prof_begin("act_quant", s);
+  if (dtype == BOOST_DT_BF16)
+    hipLaunchKernelGGL(act_quant_bf16x8_kernel, dim3(grid_for(n, 8)), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(H), static_cast<u32x4*>(S), n / 8, act);
+  else
+    hipLaunchKernelGGL(act_quant_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, H, static_cast<float*>(S),
+                       n, act);
+  prof_end(s);
+  return check_launch("act_quant");
+}
+
 int launch_colsum(const float* part, int P, int64_t stride, int64_t N, float* out, hipStream_t s) {
   // N <= 2^26 (validated dims), so the grid fits.
   const int64_t blocks = (N + kColsumCols - 1) / kColsumCols;
@@ -1153,12 +1165,12 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void
   Side* sd = nullptr;
   RBO_TRY(side_for_device(&sd));
   SideFork side(sd, s);
-  {  // dS2 = dY @ B2^T; dU2 = dS2 * act'(H2); S2 = act(H2); S1 = act(H1)
+  {  // dS2 = dY @ B2^T; dU2 = dS2 * act'(H2); S2 = act(H2)
     GemmOps ops{};
     ops.a[0] = opnd(dY, D, T, D, es);
     ops.b[0] = opnd(B2, D, r, D, es);
-    EpiDSAct::Args ea{H2, r, dU2, S2, H1, S1, d->act};
-    RBO_TRY((gemm<EpiDSAct, true, true, 1>("mlp_ds2", dt, p.ds2, T, r, D, 1, ops, ea, s)));
+    EpiDS<false>::Args ea{H2, r, r, dU2, S2, nullptr, T, nullptr, 0.f, 0.f, d->act};
+    RBO_TRY((gemm<EpiDS<false>, true, true, 1>("mlp_ds2", dt, p.ds2, T, r, D, 1, ops, ea, s)));
   }
   // Weight gradients on the side stream, each after what it reads is ready.
   RBO_TRY(side.fork());
@@ -1168,6 +1180,8 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* d, const void* x, const void
     ops.b[0] = opnd(dY, D, T, D, es);
     RBO_TRY(wgrad<TAG_MLP_DB2>("mlp_dB2", dt, p.dB2, r, D, T, 1, ops, nullptr, dB2, part, side.side()));
   }
+  // S1 = act(H1) recomputed from the saved bottleneck.
+  RBO_TRY(launch_act_quant(dt, H1, S1, T * 2 * r, d->act, s));
   // The three products of the recompute share one operand layout, K
   // contiguous: A2 already is, B1 gets a transposed copy (measured: with
   // all three M/N-major instead, B1 read as stored and A2 copied, the

@@ -255,57 +255,6 @@ struct EpiSwiglu : EpiBase {
 };
 
 // ---------------------------------------------------------------------------
-// The MLP's second bottleneck backward (no norm, one group): acc = dS2,
-// dU2 = dS2 * act'(H2), S2 = act(H2), and in the same pass the first
-// bottleneck's activation S1 = act(H1) that the recompute after it reads:
-// H1 has 2 ld columns (gate, then up), so the tile's columns lc of both
-// halves cover S1 exactly once over the product's T x ld grid. Every value
-// is rounded once to the storage dtype, as by a separate pass.
-// ---------------------------------------------------------------------------
-struct EpiDSAct : EpiBase {
-  struct Pre {
-    float h[8], g[8], u[8];
-  };
-  struct Args {
-    const float* H;    // [T][ld] fp32 (H2)
-    int64_t ld;        // columns of H, dU, S (= r)
-    void* dU;
-    void* S;
-    const float* H1;   // [T][2 ld] fp32
-    void* S1;          // [T][2 ld]
-    int act;
-  };
-  template <class C>
-  static __device__ __forceinline__ void pre(const TileCtx& c, const Args& a, int lr, int lc, Pre& pf) {
-    const int row = c.m0 + lr, col = c.n0 + lc;
-    if (row >= c.M || col >= c.N) return;
-    Vec8<float>::load(a.H, (int64_t)row * a.ld + col, pf.h);
-    Vec8<float>::load(a.H1, (int64_t)row * 2 * a.ld + col, pf.g);
-    Vec8<float>::load(a.H1, (int64_t)row * 2 * a.ld + a.ld + col, pf.u);
-  }
-  template <class C>
-  static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
-                                               const float (&v)[C::NACC][8], const Pre& pf, float&, float (&)[8]) {
-    typedef typename C::T T;
-    const int row = c.m0 + lr, col = c.n0 + lc;
-    if (row >= c.M || col >= c.N) return;
-    const int64_t o = (int64_t)row * a.ld + col, o1 = (int64_t)row * 2 * a.ld + col;
-    float du[8], sv[8], sg[8], su[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      du[e] = v[0][e] * act_grad_f(pf.h[e], a.act);
-      sv[e] = act_f(pf.h[e], a.act);
-      sg[e] = act_f(pf.g[e], a.act);
-      su[e] = act_f(pf.u[e], a.act);
-    }
-    Vec8<T>::store(a.dU, o, du);
-    Vec8<T>::store(a.S, o, sv);
-    Vec8<T>::store(a.S1, o1, sg);
-    Vec8<T>::store(a.S1, o1 + a.ld, su);
-  }
-};
-
-// ---------------------------------------------------------------------------
 // Backward through the bottleneck of group j (batch index): acc = dS_j.
 // dH = dS * act'(H), dU = rho * dH (dtype), S = act(H) recomputed (dtype,
 // optional), and per-row partials q = sum_k dH * H over this tile's columns
