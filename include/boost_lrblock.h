@@ -132,12 +132,12 @@ int boost_lrblock_fwd(const boost_lrblock_desc* desc, const void* x, const void*
 
 /* The forward above with no workspace argument, for callers that cannot
  * allocate device memory (code under stream capture, tight serving loops,
- * harnesses that forbid allocation). Its scratch (transposed weights and
- * act(H)) lives in a fixed 64 MiB array that the library holds on each
- * device it runs on until the process ends; it calls no allocator. A
+ * harnesses that forbid allocation). Its scratch (the transposed down
+ * weights and act(H)) lives in a fixed 64 MiB array that the library holds
+ * on each device it runs on until the process ends; it calls no allocator. A
  * descriptor whose forward workspace (boost_lrblock_workspace_size with
  * is_bwd = 0) exceeds 64 MiB is refused with BOOST_ERR_UNSUPPORTED (the
- * 1B-shaped QKV forward, T = 16384, d = 2048, r = 512, G = 3, needs 60 MiB).
+ * 1B-shaped QKV forward, T = 16384, d = 2048, r = 512, G = 3, needs 54 MiB).
  * Every call on a device shares that device's array: calls that may overlap
  * on one device (different streams, different host threads) race and give
  * undefined results; serialise them. Nothing in the scratch needs to start
