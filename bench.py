@@ -119,19 +119,19 @@ def recompute_flops(kind, w) -> float:
     if kind == "btp":
         return float(2 * w["T"] * w["r"] * (w["d_global"] // w["P"]))
     return 0.0
-# Weight-gradient launches: the library runs them on its side stream
-# concurrently with the input-gradient chain (the tensor-parallel share's
-# dB_s runs on the caller's stream, concurrently with dA_s on the side
-# stream), so their event durations include sharing the GPU and they are not
-# roofline candidates.
-SIDE_STREAM_LABELS = ("mlp_dB2", "mlp_dA2", "mlp1_dB", "mlp1_dA", "lrblock_dB", "lrblock_dA", "btp_dA", "btp_dB",
-                      "splitk_reduce")
+# Weight-gradient launches of the block and MLP backward: the library runs
+# them on its side stream concurrently with the input-gradient chain, so
+# their event durations include sharing the GPU and they are not roofline
+# candidates. (The tensor-parallel share runs all of its launches on the
+# caller's stream.)
+SIDE_STREAM_LABELS = ("mlp_dB2", "mlp_dA2", "mlp1_dB", "mlp1_dA", "lrblock_dB", "lrblock_dA", "splitk_reduce")
 
 
 def btp_kernel_flops(T, r, ds):
-    # btp_u_bwd: the recompute u = z @ B_s and e = dp @ A_s^T in one tile.
-    return {"btp_u": 2 * T * r * ds, "btp_p": 2 * T * ds * r,
-            "btp_u_bwd": 2 * 2 * T * r * ds, "btp_dA": 2 * ds * r * T, "btp_dB": 2 * r * ds * T,
+    # btp_u_re: the recompute u = z @ B_s; btp_u_bwd: e = dp @ A_s^T with the
+    # bottleneck backward in its epilogue.
+    return {"btp_u": 2 * T * r * ds, "btp_p": 2 * T * ds * r, "btp_u_re": 2 * T * r * ds,
+            "btp_u_bwd": 2 * T * r * ds, "btp_dA": 2 * ds * r * T, "btp_dB": 2 * r * ds * T,
             "btp_dz": 2 * T * ds * r}
 
 

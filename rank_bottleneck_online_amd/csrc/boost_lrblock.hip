@@ -799,11 +799,10 @@ int btp_check_desc(const boost_btp_share_desc* d) {
 }
 
 struct BtpPlan {
-  Choice u, p, ue, dA, dB, dz;
+  Choice u, p, e, dA, dB, dz;
   size_t f_ag, f_sp, fwd_bytes;
-  // dA_s and dB_s run on different streams, so their split-K partials get
-  // separate buffers.
-  size_t b_BT, b_du, b_ag, b_dg, b_part_dA, b_part_dB, bwd_bytes;
+  // dA_s and dB_s run one after the other and share the split-K partials.
+  size_t b_U, b_du, b_ag, b_dg, b_part, bwd_bytes;
   size_t fwd_largest, bwd_largest;
 };
 
@@ -813,7 +812,7 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   const int64_t T = d->T, r = d->r, S = d->d_shard, es = esize(dt);
   p.u = choose(dt, T, S, r, 1, false, false, true);
   p.p = choose(dt, T, r, S, 1, false, false, true);
-  p.ue = choose(dt, T, S, r, 1, false, true);
+  p.e = choose(dt, T, S, r, 1, false, false, true);
   p.dA = choose(dt, S, r, T, 1, true, false);
   p.dB = choose(dt, r, S, T, 1, true, false);
   p.dz = choose(dt, T, r, S, 1, false, false, true, true);
@@ -823,12 +822,13 @@ BtpPlan btp_plan(const boost_btp_share_desc* d) {
   p.fwd_bytes = f.total;
   p.fwd_largest = f.largest;
   WsLayout b;
-  p.b_BT = b.take((size_t)(r * S * es));
+  p.b_U = b.take((size_t)(T * S * 4));
   p.b_du = b.take((size_t)(T * S * es));
   p.b_ag = b.take((size_t)(T * S * es));
-  p.b_dg = b.take((size_t)(p.ue.tiles_m * S * 4));
-  p.b_part_dA = p.dA.splits > 1 ? b.take((size_t)(p.dA.splits * S * r * 4)) : 0;
-  p.b_part_dB = p.dB.splits > 1 ? b.take((size_t)(p.dB.splits * r * S * 4)) : 0;
+  p.b_dg = b.take((size_t)(p.e.tiles_m * S * 4));
+  const size_t part = std::max(p.dA.splits > 1 ? (size_t)(p.dA.splits * S * r * 4) : (size_t)0,
+                               p.dB.splits > 1 ? (size_t)(p.dB.splits * r * S * 4) : (size_t)0);
+  p.b_part = part ? b.take(part) : 0;
   p.bwd_bytes = b.total;
   p.bwd_largest = b.largest;
   return p;
@@ -1304,20 +1304,27 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
   void* du = at(ws, p.b_du);
   void* ag = at(ws, p.b_ag);
   float* dgp = reinterpret_cast<float*>(at(ws, p.b_dg));
-  float* part_dA = p.b_part_dA ? reinterpret_cast<float*>(at(ws, p.b_part_dA)) : nullptr;
-  float* part_dB = p.b_part_dB ? reinterpret_cast<float*>(at(ws, p.b_part_dB)) : nullptr;
-  void* BT = at(ws, p.b_BT);
-  RBO_TRY(launch_transposes(dt, {{B_s, nullptr, BT, r, S, 1}}, st));
-  {  // recompute u = z @ B_s and e = dp @ A_s^T in the same tile; du, ag, dg partials
+  float* U = reinterpret_cast<float*>(at(ws, p.b_U));
+  float* part = p.b_part ? reinterpret_cast<float*>(at(ws, p.b_part)) : nullptr;
+  // u and e = dp @ A_s^T in two launches of one-round tiles (192 x 256: 215
+  // tiles each, against 320 two-accumulator tiles of 256 x 128 in 1.25
+  // rounds), u handed over in fp32 so the results are those of one tile
+  // holding both accumulators; B_s is read as stored.
+  {  // u = z @ B_s recomputed, kept in fp32
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);
-    ops.b[0] = opnd(BT, r, S, r, es);
-    ops.a[1] = opnd(dp, r, T, r, es);
-    ops.b[1] = opnd(A_s, r, S, r, es);
-    EpiBtpUBwd::Args ea{ds, g_s, du, ag, dgp, S};
-    RBO_TRY((gemm<EpiBtpUBwd, true, true, 2>("btp_u_bwd", dt, p.ue, T, S, r, 1, ops, ea, st)));
+    ops.b[0] = opnd(B_s, S, r, S, es);
+    EpiStore<true>::Args ea{U, S, 0, nullptr};
+    RBO_TRY((gemm<EpiStore<true>, true, false, 1>("btp_u_re", dt, p.u, T, S, r, 1, ops, ea, st)));
   }
-  RBO_TRY(launch_colsum(dgp, p.ue.tiles_m, S, S, dg_s, st));
+  {  // e = dp @ A_s^T; du, ag, dg partials
+    GemmOps ops{};
+    ops.a[0] = opnd(dp, r, T, r, es);
+    ops.b[0] = opnd(A_s, r, S, r, es);
+    EpiBtpEBwd::Args ea{ds, g_s, U, du, ag, dgp, S};
+    RBO_TRY((gemm<EpiBtpEBwd, true, true, 1>("btp_u_bwd", dt, p.e, T, S, r, 1, ops, ea, st)));
+  }
+  RBO_TRY(launch_colsum(dgp, p.e.tiles_m, S, S, dg_s, st));
   // dz, dA_s and dB_s in a row on the caller's stream. Measured on the 13B
   // share (three products of 8192 x 1280 x 1280 that each fill most of the
   // GPU): 0.305-0.310 ms per step this way, against 0.314-0.318 ms with dA_s
@@ -1334,13 +1341,13 @@ int boost_btp_share_bwd(const boost_btp_share_desc* d, const void* z, const void
     GemmOps ops{};
     ops.a[0] = opnd(ag, S, T, S, es);
     ops.b[0] = opnd(dp, r, T, r, es);
-    RBO_TRY(wgrad<TAG_BTP_DA>("btp_dA", dt, p.dA, S, r, T, 1, ops, nullptr, dA_s, part_dA, st));
+    RBO_TRY(wgrad<TAG_BTP_DA>("btp_dA", dt, p.dA, S, r, T, 1, ops, nullptr, dA_s, part, st));
   }
   {  // dB_s = z^T @ du
     GemmOps ops{};
     ops.a[0] = opnd(z, r, T, r, es);
     ops.b[0] = opnd(du, S, T, S, es);
-    RBO_TRY(wgrad<TAG_BTP_DB>("btp_dB", dt, p.dB, r, S, T, 1, ops, nullptr, dB_s, part_dB, st));
+    RBO_TRY(wgrad<TAG_BTP_DB>("btp_dB", dt, p.dB, r, S, T, 1, ops, nullptr, dB_s, part, st));
   }
   return BOOST_OK;
 }

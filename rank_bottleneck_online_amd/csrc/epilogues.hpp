@@ -509,26 +509,25 @@ struct EpiBtpP : EpiBase {
 };
 
 // ---------------------------------------------------------------------------
-// Tensor-parallel share, backward: two accumulators over the same [T, d_s]
-// tile, the recompute u = z @ B_s and e = dp @ A_s^T (both K = r; e never
-// leaves the fp32 registers), fused with the backward of SiLU, the gain and
-// the local statistic:
-//   a = SiLU(u); da = g_s e + 2 ds a; du = da SiLU'(u)
-// writes du (dtype), a * g_s (dtype, operand of dA_s) and per-column
-// partials of dg_s = sum_t a e over this tile's rows.
+// BTP share backward through the bottleneck: acc = e = dp @ A_s^T, with
+// u = z @ B_s recomputed by the launch before it and stored in fp32 (the
+// value its accumulator held). a = SiLU(u), da = g_s * e + 2 ds a (the
+// statistic's gradient), du = da * SiLU'(u), ag = a * g_s (the operand of
+// dA_s), and column partials of a * e (dg_s) per tile row.
 // ---------------------------------------------------------------------------
-struct EpiBtpUBwd : EpiBase {
+struct EpiBtpEBwd : EpiBase {
   static constexpr bool kColSum = true;
   struct Pre {
-    float g[8];
+    float g[8], u[8];
   };
   struct Args {
     const float* ds;
     const void* g;
+    const float* U;   // [T][ld] fp32
     void* du;
     void* ag;
-    float* dgpart;  // [tiles_m][ld]
-    int64_t ld;     // d_shard
+    float* dgpart;    // [tiles_m][ld]
+    int64_t ld;       // d_shard
   };
   template <class C>
   static __device__ __forceinline__ void begin(const TileCtx& c, const Args& a) {
@@ -540,26 +539,26 @@ struct EpiBtpUBwd : EpiBase {
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
     Vec8<T>::load(a.g, col, pf.g);
+    Vec8<float>::load(a.U, (int64_t)row * a.ld + col, pf.u);
   }
   template <class C>
   static __device__ __forceinline__ void apply(const TileCtx& c, const Args& a, int lr, int lc,
                                                const float (&v)[C::NACC][8], const Pre& pf, float&, float (&colc)[8]) {
     typedef typename C::T T;
-    static_assert(C::NACC == 2, "the share's backward takes the u and e accumulators");
+    static_assert(C::NACC == 1, "one accumulator: e");
     const int row = c.m0 + lr, col = c.n0 + lc;
     if (row >= c.M || col >= c.N) return;
     const int64_t o = (int64_t)row * a.ld + col;
     const float dsv = c.rowv[lr];
     float du[8], ag[8];
-    const float (&gv)[8] = pf.g;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float u = v[0][e], ev = v[1][e];
+      const float u = pf.u[e], ev = v[0][e];
       const float s = sigmoid_f(u);
       const float av = u * s;
-      const float da = gv[e] * ev + 2.f * dsv * av;
+      const float da = pf.g[e] * ev + 2.f * dsv * av;
       du[e] = da * (s * (1.f + u * (1.f - s)));
-      ag[e] = av * gv[e];
+      ag[e] = av * pf.g[e];
       colc[e] += av * ev;
     }
     Vec8<T>::store(a.du, o, du);

@@ -42,8 +42,8 @@ def test_btp_share_flops_are_three_forwards_plus_the_recompute():
     k = bench.btp_kernel_flops(w["T"], w["r"], ds)
     fwd = k["btp_u"] + k["btp_p"]
     assert sum(k.values()) == 3 * fwd + bench.recompute_flops("btp", w)
-    # the u recompute and e = dp A_s^T share one launch
-    assert k["btp_u_bwd"] == 2 * k["btp_u"]
+    # the u recompute and e = dp A_s^T are one product each
+    assert k["btp_u_re"] == k["btp_u_bwd"] == k["btp_u"]
 
 
 def test_lrblock_backward_is_twice_the_forward():
