@@ -497,9 +497,37 @@ def lrblock_fwd_kernel_rw(T, d, r, G, d_out):
             "lrblock_up": (T * G * r * b + G * r * d_out * b, G * T * d_out * b)}
 
 
+# The tensor-parallel share: every launch has an instantiation of its own.
+BTP_LABEL_PATTERNS = {
+    "btp_u": "NS_7EpiBtpUE",
+    "btp_p": "NS_7EpiBtpPE",
+    "btp_u_re": "NS_8EpiStoreILb1EEELi0EE",
+    "btp_u_bwd": "NS_10EpiBtpEBwdE",
+    "btp_dz": "NS_8EpiStoreILb0EEELi0EE",
+    "btp_dA": "NS_8EpiStoreILb1EEELi5EE",
+    "btp_dB": "NS_8EpiStoreILb1EEELi6EE",
+}
+
+
+def btp_kernel_rw(T, r, S):
+    """(read, written) algorithmic bytes of the share's launches (bf16
+    operands; fp32 statistic, u handed over in fp32, fp32 weight gradients)."""
+    b, f = 2, 4
+    return {"btp_u": (T * r * b + r * S * b + S * b, T * S * b + T * f),
+            "btp_p": (T * S * b + S * r * b, T * r * b + T * f),
+            "btp_u_re": (T * r * b + r * S * b, T * S * f),
+            "btp_u_bwd": (T * r * b + S * r * b + T * S * f + S * b + T * f, 2 * T * S * b),
+            "btp_dz": (T * S * b + r * S * b, T * r * b),
+            "btp_dA": (T * S * b + T * r * b, S * r * f),
+            "btp_dB": (T * r * b + T * S * b, r * S * f)}
+
+
 def counter_workload(workload: str):
     """(label patterns, {label: flops}, {label: (read, written)}) of a
-    workload whose launches the counter summaries cover."""
+    workload whose launches the counter summaries attribute to labels, or
+    (None, {}, {}) for one whose kernel instantiations serve several
+    launches (the chained layer and the layer set): those are summarised
+    per instantiation."""
     w = synth.WORKLOADS[workload]
     if w["kind"] == "lrmlp":
         a = {k: w[k] for k in ("T", "d", "r", "ffn")}
@@ -507,7 +535,18 @@ def counter_workload(workload: str):
     if w["kind"] == "lrblock" and workload.endswith("_fwd"):
         return (LRBLOCK_FWD_LABEL_PATTERNS, lrblock_kernel_flops(w["T"], w["d"], w["r"], w["G"], w["d_out"], False),
                 lrblock_fwd_kernel_rw(w["T"], w["d"], w["r"], w["G"], w["d_out"]))
-    raise SystemExit(f"counter summaries cover the 7B MLP and the QKV forward, not {workload}")
+    if w["kind"] == "btp":
+        S = w["d_global"] // w["P"]
+        return BTP_LABEL_PATTERNS, btp_kernel_flops(w["T"], w["r"], S), btp_kernel_rw(w["T"], w["r"], S)
+    if w["kind"] in ("layer", "layerset"):
+        return None, {}, {}
+    raise SystemExit(f"no counter summary for workload {workload}")
+
+
+def instantiation_patterns(*per_kernel_maps):
+    """{short name: full name} of every GEMM instantiation in counter maps."""
+    names = sorted({k for m in per_kernel_maps for k in m if "gemm_kernel" in k})
+    return {short_kernel_name(k): k for k in names}
 
 
 def short_kernel_name(n: str) -> str:
@@ -571,9 +610,22 @@ def mfma_summary(csv_path: str, title: str, command: str, workload: str = "llama
     util = counter_per_kernel(csv_path, "MfmaUtil")
     mops = counter_per_kernel(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
     patterns, kf, _ = counter_workload(workload)
-    out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
-           "| launch | kernel | MFMA busy (% of SIMD cycles) | counted MFMA GF | algorithmic GF | counted / algorithmic |",
-           "|---|---|---|---|---|---|"]
+    out = [f"# {title}", "", "Command:", "", "```", command, "```", ""]
+    if patterns is None:
+        # Instantiations shared by several launches: per-dispatch means over
+        # every launch an instantiation served (several shapes).
+        out += ["One row per kernel instantiation; an instantiation that serves several launches of the step "
+                "(e.g. the weight gradients of the QKV, O and MLP blocks) averages over all of them.", "",
+                "| kernel | dispatches | MFMA busy (% of SIMD cycles, mean) | counted MFMA GF per dispatch (mean) |",
+                "|---|---|---|---|"]
+        for short, full in instantiation_patterns(util, mops).items():
+            u, m = util.get(full), mops.get(full)
+            if not u or not m:
+                continue
+            out.append(f"| {short} | {len(u)} | {sum(u) / len(u):.1f} | {sum(m) / len(m) * 512 / 1e9:.1f} |")
+        return "\n".join(out) + "\n"
+    out += ["| launch | kernel | MFMA busy (% of SIMD cycles) | counted MFMA GF | algorithmic GF | counted / algorithmic |",
+            "|---|---|---|---|---|---|"]
     for label, pat in patterns.items():
         un = [k for k in util if pat in k]
         mn = [k for k in mops if pat in k]
@@ -604,6 +656,8 @@ def traffic_json(fetch_csv: str, write_csv: str, workload: str, copy_mib: int) -
     f_scale, w_scale = known / (fk * 1024.0), known / (wk * 1024.0)
     kernels = {}
     patterns = counter_workload(workload)[0]
+    if patterns is None:
+        patterns = instantiation_patterns(fetch, write)
     for label, pat in patterns.items():
         fn = [k for k in fetch if pat in k]
         wn = [k for k in write if pat in k]
@@ -635,7 +689,9 @@ def traffic_table(json_path: str, title: str, command: str) -> str:
            "last-level (MALL) cache count too: fetched bytes are upper bounds on DRAM bytes.", "",
            f"Source digest of the kernels measured: `{tj['source_digest']}`.", "",
            "Algorithmic bytes: each input read once, each output written once (the operands of every launch are "
-           "listed in `mlp_kernel_rw` / `lrblock_fwd_kernel_rw` in bench.py). Fetched bytes above the algorithmic "
+           "listed in `mlp_kernel_rw`, `lrblock_fwd_kernel_rw` and `btp_kernel_rw` in bench.py; a workload whose "
+           "kernel instantiations serve several launches is listed per instantiation, as means over its "
+           "dispatches, without algorithmic bytes). Fetched bytes above the algorithmic "
            "reads are operand panels "
            "that many tiles share and that leave an XCD's 4 MB L2 between the waves of tiles using them (the "
            "up projections and the recompute, with K = r, re-read their S1/B1 panels once per wave of tiles); "
@@ -647,15 +703,20 @@ def traffic_table(json_path: str, title: str, command: str) -> str:
            "fetched / algorithmic read | us (profiled) | counted GB/s | % of HBM peak | algorithmic GB/s |",
            "|---|---|---|---|---|---|---|---|---|---|---|"]
     for label, k in tj["kernels"].items():
-        rd, wr = rw[label]
+        # Per-instantiation rows (shared by launches of several shapes) have
+        # no algorithmic bytes of their own.
+        rd, wr = rw.get(label, (None, None))
         ms = k.get("avg_ms_profiled")
+        alg = "- | - | -" if rd is None else f"{rd / 1e6:.0f} | {wr / 1e6:.0f} | {k['fetch_bytes'] / rd:.2f}"
         if ms:
             cg = (k["fetch_bytes"] + k["write_bytes"]) / (ms * 1e-3) / 1e9
-            rates = f"{ms * 1e3:.1f} | {cg:.0f} | {100 * cg / PEAK_HBM_GBS:.1f} | {(rd + wr) / (ms * 1e-3) / 1e9:.0f}"
+            ag = "-" if rd is None else f"{(rd + wr) / (ms * 1e-3) / 1e9:.0f}"
+            rates = f"{ms * 1e3:.1f} | {cg:.0f} | {100 * cg / PEAK_HBM_GBS:.1f} | {ag}"
         else:
             rates = "- | - | - | -"
-        out.append(f"| {label} | {k['kernel']} | {k['fetch_bytes'] / 1e6:.0f} | {k['write_bytes'] / 1e6:.0f} | "
-                   f"{rd / 1e6:.0f} | {wr / 1e6:.0f} | {k['fetch_bytes'] / rd:.2f} | {rates} |")
+        kern = k["kernel"] if k["kernel"] != label else f"mean of {k['dispatches']} dispatches"
+        out.append(f"| {label} | {kern} | {k['fetch_bytes'] / 1e6:.0f} | {k['write_bytes'] / 1e6:.0f} | "
+                   f"{alg} | {rates} |")
     return "\n".join(out) + "\n"
 
 def r_sweep(B, torch, ranks, steps, warmup):
@@ -695,7 +756,11 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--split-steps", type=int, default=10,
+                    help="steps of the untimed pass that splits forward and backward with events (default 10)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: as many as fill --warmup-s seconds, at least 3)")
+    ap.add_argument("--warmup-s", type=float, default=0.5, help="seconds of warm-up when --warmup is not given")
     ap.add_argument("--workload", default="llama2_7b_mlp", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--act", default=None, help="bottleneck activation for the layer set (silu|identity)")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
@@ -758,7 +823,8 @@ def main():
     B.lib()
 
     if args.r_sweep:
-        r_sweep(B, torch, [int(v) for v in args.r_sweep.split(",")], args.steps, args.warmup)
+        r_sweep(B, torch, [int(v) for v in args.r_sweep.split(",")], args.steps,
+                3 if args.warmup is None else args.warmup)
         return
 
     wl = Workload(args.workload)
@@ -776,8 +842,21 @@ def main():
         log(f"calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
 
-    for _ in range(args.warmup):
-        wl.step()
+    # Warm-up: W steps, or by default as many as fill --warmup-s seconds (at
+    # least 3). From idle the GPU needs tens of milliseconds under load to
+    # reach its working clock, longer than a few steps of the smaller
+    # workloads (a 0.25 ms step timed after 3 warm-up steps reads 15% slow).
+    if args.warmup is None:
+        warmup, t_end = 0, time.perf_counter() + args.warmup_s
+        while warmup < 3 or time.perf_counter() < t_end:
+            wl.step()
+            warmup += 1
+            if warmup % 8 == 0:
+                torch.cuda.synchronize()  # the host stays within 8 steps of the GPU
+    else:
+        warmup = args.warmup
+        for _ in range(warmup):
+            wl.step()
     torch.cuda.synchronize()
 
     # Which kernel dominates the step (untimed discovery pass).
@@ -794,28 +873,41 @@ def main():
     log("kernel times in one step (ms):", json.dumps({k: round(v, 4) for k, v in
                                                        sorted(per_kernel.items(), key=lambda kv: -kv[1])}))
 
-    # Timed region: K steps, HIP events around the dominant kernel's launches
-    # and at every forward/backward boundary (fwd and bwd split, median, min).
+    # Timed region: K steps between two events, plus the library's events
+    # around the dominant kernel's launches (created without the system-scope
+    # fence, so they cost the stream almost nothing).
     B.profiler_enable(dom, 64 * max(1, args.steps))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev[0].record(stream)
+    e_start.record(stream)
     for i in range(args.steps):
+        wl.step()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e_start.elapsed_time(e_end) / args.steps
+    rep = B.profiler_report()
+    B.profiler_disable()
+
+    # Forward / backward split, not part of `value`: a separate pass with an
+    # event at every boundary. An event recorded on the stream costs it a few
+    # microseconds (its cache write-back), which is why these stay out of the
+    # timed region; the split's step times include them.
+    n_split = max(1, min(args.steps, args.split_steps))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_split + 1)]
+    ev[0].record(stream)
+    for i in range(n_split):
         wl.fwd()
         ev[2 * i + 1].record(stream)
         if wl.bwd_fn is not None:
             wl.bwd_fn()
         ev[2 * i + 2].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev[0].elapsed_time(ev[2 * args.steps]) / args.steps
-    fwd_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
-    bwd_ms = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)]
+    fwd_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_split)]
+    bwd_ms = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(n_split)]
     step_ms = [a + b for a, b in zip(fwd_ms, bwd_ms)]
-    rep = B.profiler_report()
-    B.profiler_disable()
 
     # Second pass, not part of `value`: the 256 MB last-level cache is flushed
     # (a 512 MB buffer is written) before every step, so inputs come from HBM.
@@ -937,7 +1029,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -951,7 +1043,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "timing": {"step_ms_median": round(med(step_ms), 4), "step_ms_min": round(min(step_ms), 4),
+        "timing": {"split_steps": n_split,
+                   "step_ms_median": round(med(step_ms), 4), "step_ms_min": round(min(step_ms), 4),
                    "fwd_ms_median": round(med(fwd_ms), 4), "fwd_ms_min": round(min(fwd_ms), 4),
                    "bwd_ms_median": round(med(bwd_ms), 4) if wl.bwd_fn else None,
                    "bwd_ms_min": round(min(bwd_ms), 4) if wl.bwd_fn else None,

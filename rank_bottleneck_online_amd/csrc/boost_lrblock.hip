@@ -5,6 +5,7 @@
 // The library allocates no device memory and never synchronises a stream
 // (except inside boost_profiler_report, which waits on its own events).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -80,6 +81,17 @@ void prof_end(hipStream_t s) {
   if (t_prof_pending < 0) return;
   if (hipEventRecord(g_prof.recs[t_prof_pending].stop, s) == hipSuccess) ++g_prof.used;
   t_prof_pending = -1;
+}
+// A single-kernel launch that the timer covers takes the record's events on
+// the dispatch itself (the extended launch stamps them with the kernel's own
+// start and end): the timed duration is the kernel's alone, as a kernel
+// trace reports it, and no marker packet enters the stream.
+ProfRec* prof_claim(const char* label) {
+  if (!g_prof.on || g_prof.used >= g_prof.recs.size()) return nullptr;
+  if (!g_prof.filter.empty() && !strstr(label, g_prof.filter.c_str())) return nullptr;
+  ProfRec& r = g_prof.recs[g_prof.used];
+  r.label = label;
+  return &r;
 }
 
 // ---------------------------------------------------------------------------
@@ -190,11 +202,15 @@ int launch_cfg(const char* label, const Choice& ch, int M, int N, int K, int bat
       hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<C, E, TAG>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   (void)attr;
-  prof_begin(label, s);
-  hipLaunchKernelGGL((gemm_kernel<C, E, TAG>), dim3((unsigned)grid), dim3(C::NT), C::LDS_BYTES, s, g, ops, ea);
+  ProfRec* pr = prof_claim(label);
+  if (pr)
+    hipExtLaunchKernelGGL((gemm_kernel<C, E, TAG>), dim3((unsigned)grid), dim3(C::NT), C::LDS_BYTES, s, pr->start,
+                          pr->stop, 0, g, ops, ea);
+  else
+    hipLaunchKernelGGL((gemm_kernel<C, E, TAG>), dim3((unsigned)grid), dim3(C::NT), C::LDS_BYTES, s, g, ops, ea);
   const hipError_t e = hipGetLastError();
-  prof_end(s);
   if (e != hipSuccess) return fail(BOOST_ERR_LAUNCH, "%s: %s", label, hipGetErrorString(e));
+  if (pr) ++g_prof.used;
   return BOOST_OK;
 }
 
@@ -1415,11 +1431,14 @@ int boost_profiler_enable(const char* name_filter, int max_records) {
   g_prof.recs.reserve((size_t)max_records);
   for (int i = 0; i < max_records; ++i) {
     ProfRec r{"", nullptr, nullptr};
-    if (hipEventCreate(&r.start) != hipSuccess) {
+    // Timing-only events: without the system-scope fence a record does not
+    // write back and invalidate the caches, so the events barely perturb the
+    // stream they time.
+    if (hipEventCreateWithFlags(&r.start, hipEventDisableSystemFence) != hipSuccess) {
       boost_profiler_disable();
       return fail(BOOST_ERR_LAUNCH, "hipEventCreate failed");
     }
-    if (hipEventCreate(&r.stop) != hipSuccess) {
+    if (hipEventCreateWithFlags(&r.stop, hipEventDisableSystemFence) != hipSuccess) {
       hipEventDestroy(r.start);
       boost_profiler_disable();
       return fail(BOOST_ERR_LAUNCH, "hipEventCreate failed");

@@ -70,6 +70,49 @@ def test_each_mlp_label_names_one_kernel():
         assert len(hits) == 1, (lab, hits)
 
 
+def _gemm_name(cfg, epi, tag=0):
+    return f"_ZN3rbo11gemm_kernelINS_3CfgIDF16b{cfg}EEENS_{epi}ELi{tag}EEEvNS_8GemmGeomENS_7GemmOpsENT0_4ArgsE"
+
+
+def test_each_btp_label_names_one_kernel():
+    """The tensor-parallel share's seven launches run seven distinct kernel
+    instantiations, and each label pattern picks out exactly its own."""
+    kcnc, kckc, mcnc = "Li192ELi256ELi2ELi4ELb1ELb0ELi1", "Li192ELi256ELi2ELi4ELb1ELb1ELi1", "Li128ELi128ELi2ELi4ELb0ELb0ELi1"
+    step = {"btp_u": _gemm_name(kcnc, "7EpiBtpU"), "btp_p": _gemm_name(kcnc, "7EpiBtpP"),
+            "btp_u_re": _gemm_name(kcnc, "8EpiStoreILb1EE"), "btp_u_bwd": _gemm_name(kckc, "10EpiBtpEBwd"),
+            "btp_dz": _gemm_name(kckc, "8EpiStoreILb0EE"), "btp_dA": _gemm_name(mcnc, "8EpiStoreILb1EE", 5),
+            "btp_dB": _gemm_name(mcnc, "8EpiStoreILb1EE", 6)}
+    assert set(bench.BTP_LABEL_PATTERNS) == set(step)
+    for lab, pat in bench.BTP_LABEL_PATTERNS.items():
+        hits = [k for k, n in step.items() if pat in n]
+        assert hits == [lab], (lab, hits)
+    patterns, flops, rw = bench.counter_workload("llama2_13b_btp_share_tp4")
+    assert set(flops) == set(rw) == set(patterns)
+    # e.g. dz = du B_s^T reads du [T, S] and B_s [r, S] in bf16, writes dz [T, r]
+    w = synth.WORKLOADS["llama2_13b_btp_share_tp4"]
+    T, r, S = w["T"], w["r"], w["d_global"] // w["P"]
+    assert rw["btp_dz"] == (2 * (T * S + r * S), 2 * T * r)
+
+
+def test_shared_instantiations_are_summarised_per_kernel(tmp_path):
+    """The chained layer's weight-gradient instantiation serves several
+    launches: the MFMA table lists it once, with its dispatch count and
+    per-dispatch means."""
+    assert bench.counter_workload("llama2_40b_layer_chained")[0] is None
+    path = str(tmp_path / "m.csv")
+    rows = []
+    for util, mops in ((40.0, 1e9), (60.0, 3e9)):
+        rows += [(WGRAD, "MfmaUtil", util), (WGRAD, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops)]
+    rows += [(DOWN1, "MfmaUtil", 50.0), (DOWN1, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2e9),
+             ("rbo::colsum_kernel", "MfmaUtil", 0.0)]
+    _counter_csv(path, rows)
+    table = bench.mfma_summary(path, "t", "c", "llama2_40b_layer_chained")
+    body = [ln for ln in table.splitlines() if ln.startswith("| gemm")]
+    assert len(body) == 2
+    wg = [c.strip() for c in [ln for ln in body if "tag 4" in ln][0].strip("|").split("|")]
+    assert wg[1] == "2" and wg[2] == "50.0" and wg[3] == f"{2e9 * 512 / 1e9:.1f}"
+
+
 def _counter_csv(path, rows):
     with open(path, "w", newline="") as f:
         wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
