@@ -38,10 +38,12 @@
 // K tail of K = tokens products need no branches. Reads past M or N inside
 // the tensor only feed accumulator rows/columns that the epilogue masks.
 //
-// Pipelining. As many LDS stages as fit (two for 256 x 256 tiles, three or
-// four for smaller ones): while the MFMAs read stage kt, the slabs of the
-// next NSTAGE-1 steps are in flight, and each step waits only for the
-// oldest. The load instructions of the next slab are interleaved one by one
+// Pipelining. As many LDS stages as fit (three or four for tiles smaller
+// than 256 x 256): while the MFMAs read stage kt, the slabs of the next
+// NSTAGE-1 steps are in flight, and each step waits only for the oldest.
+// 256 x 256 tiles, where two whole slabs fit, stage half-slabs (one
+// operand's panel of a K step) in a ring of five instead, which keeps one
+// and a half slabs in flight. The load instructions of the next slab are interleaved one by one
 // with the MFMAs of the first two k sub-steps, so that a stalled load issue
 // never leaves the matrix cores idle (with one wave per SIMD there is no
 // other wave to fill the gap). MFMA fragments are double-buffered across
@@ -75,6 +77,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kRowBytes = 128;  // bytes of K per staged tile row
+// Square tiles whose whole-slab stages fit only twice (256 x 256) stage
+// half-slabs in a ring of five instead (see the kernel's main loop).
+constexpr bool kHalfSlabRing = true;
 
 __device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -179,7 +184,10 @@ struct Cfg {
   static constexpr int FIT_ = (160 * 1024 - VEC_BYTES_) / STAGE_BYTES;
   static constexpr int NSTAGE = FIT_ < 4 ? FIT_ : 4;
   static_assert(NSTAGE >= 2, "two pipeline stages must fit in LDS");
-  static constexpr int PIPE_BYTES = NSTAGE * STAGE_BYTES;
+  // Half-slab ring: five panels (an A or a B panel of one K step, A_BYTES
+  // each) fill the 160 KB, against two whole slabs plus the vectors.
+  static constexpr bool RING = kHalfSlabRing && BM == BN && NACC == 1 && NSTAGE == 2 && 5 * BM * RB <= 160 * 1024;
+  static constexpr int PIPE_BYTES = RING ? 5 * A_BYTES : NSTAGE * STAGE_BYTES;
   // Epilogue staging: each wave writes 32 accumulator rows at a time (per
   // accumulator) into a private fp32 buffer with a row stride padded by 8
   // floats (the two half-waves of the MFMA layout then hit disjoint banks;
@@ -192,8 +200,12 @@ struct Cfg {
   static constexpr int EPI_BYTES = WM * WN * NACC * EPI_SUB * 4;
   static constexpr int SCR_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
   // After that: per-row / per-column fp32 vectors and reduction partials.
+  // They are used only after the main loop, so with the ring they sit in
+  // the pipeline space, past the epilogue staging.
   static constexpr int VEC_BYTES = VEC_BYTES_;
-  static constexpr int LDS_BYTES = SCR_BYTES + VEC_BYTES;
+  static constexpr int VEC_OFF = RING ? EPI_BYTES : SCR_BYTES;
+  static_assert(!RING || EPI_BYTES + VEC_BYTES <= PIPE_BYTES, "ring: vectors must fit past the staging");
+  static constexpr int LDS_BYTES = RING ? PIPE_BYTES : SCR_BYTES + VEC_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "tile does not fit the LDS of a CU");
   static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA block");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
@@ -696,44 +708,88 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
     if constexpr (decltype(a_tag)::value) DA::issue(ra[Q], lda_b[Q], k0, st, wave, lane, oob);
     if constexpr (decltype(b_tag)::value) DB::issue(rb[Q], ldb_b[Q], k0, st + C::A_BYTES, wave, lane, oob);
   };
-  static_for<0, NS - 1>([&](auto s) {
-    issue(std::integral_constant<int, 0>{}, s(), smem + s() * C::STAGE_BYTES, std::true_type{}, std::true_type{});
-  });
-  int cur = 0;       // stage read in this step
-  int nxt = NS - 1;  // stage refilled in this step
-  // One K step on pair p whose loads fetch slab k of pair Q.
-  auto step = [&](auto p, auto q_tag, int k) {
-    // Slabs of the next NS-1 steps are in flight; wait for this one only.
-    wait_vmcnt<L * (NS - 2)>();
-    // A plain s_barrier: __syncthreads() would add a release fence that
-    // waits for every outstanding load, including the slabs still allowed
-    // in flight. The empty asm statements keep the compiler from moving
-    // LDS accesses across the barrier.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // The slab NS-1 steps ahead goes to the stage last read in the
-    // previous step, which every wave has finished once past the barrier.
-    char* st = smem + nxt * C::STAGE_BYTES;
-    const char* As = smem + cur * C::STAGE_BYTES;
-    compute(p, As, As + C::A_BYTES, Plan{}, [&](auto kk) {
-      issue(q_tag, k, st, std::bool_constant<kk == Plan::A_AT>{}, std::bool_constant<kk == Plan::B_AT>{});
+  if constexpr (C::RING) {
+    // Half-slab ring. K step k's panels are A_k and B_k; panel h of the
+    // sequence A_0, B_0, A_1, B_1, ... lives in slot h mod 5. Step k reads
+    // slots 2k, 2k+1 and issues B_{k+1} in its first sub-step (it is needed
+    // next) and A_{k+2} in its second, into slots 2k+3 and 2k+4 (mod 5):
+    // those held A_{k-1} and B_{k-1}, which every wave has finished once past
+    // the step's barrier. One and a half slabs stay in flight, against one
+    // with two whole-slab stages, and the wait at the top of a step lets the
+    // newest panel (A_{k+1}) stay outstanding. Issue order A_0, B_0, A_1,
+    // then two panels per step; with in-order completion, vmcnt(DA::INSTR)
+    // at the top of step k means A_k and B_k have landed.
+    static_assert(C::A_BYTES == C::B_BYTES && C::NACC == 1, "ring: square single-accumulator tiles");
+    constexpr int HB = C::A_BYTES;
+    auto panel = [&](auto is_a, int k, char* dst) {
+      const bool live = k < KT;
+      const uint32_t oob = live ? 0u : 0x80000000u;
+      int kr = k + krot;
+      kr = kr >= KT ? kr - KT : kr;
+      const int k0 = kbeg + (live ? kr : 0) * C::BK;
+      if constexpr (decltype(is_a)::value) DA::issue(ra[0], lda_b[0], k0, dst, wave, lane, oob);
+      else DB::issue(rb[0], ldb_b[0], k0, dst, wave, lane, oob);
+    };
+    panel(std::true_type{}, 0, smem);
+    panel(std::false_type{}, 0, smem + HB);
+    panel(std::true_type{}, 1, smem + 2 * HB);
+    int h = 0;  // slot of A_k
+    const int KTr = KT > 1 ? KT : 1;
+    for (int k = 0; k < KTr; ++k) {
+      wait_vmcnt<DA::INSTR>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int hb = h == 4 ? 0 : h + 1;  // B_k
+      const int fb = h >= 2 ? h - 2 : h + 3;  // B_{k+1}
+      const int fa = h >= 1 ? h - 1 : h + 4;  // A_{k+2}
+      compute(std::integral_constant<int, 0>{}, smem + h * HB, smem + hb * HB, SlabPlan<DA::INSTR, 1, DB::INSTR, 0>{},
+              [&](auto kk) {
+                if constexpr (kk == 0) panel(std::false_type{}, k + 1, smem + fb * HB);
+                else panel(std::true_type{}, k + 2, smem + fa * HB);
+              });
+      h = h >= 3 ? h - 3 : h + 2;
+    }
+  } else {
+    static_for<0, NS - 1>([&](auto s) {
+      issue(std::integral_constant<int, 0>{}, s(), smem + s() * C::STAGE_BYTES, std::true_type{}, std::true_type{});
     });
-    cur = cur + 1 == NS ? 0 : cur + 1;
-    nxt = nxt + 1 == NS ? 0 : nxt + 1;
-  };
-  static_for<0, C::NACC>([&](auto p) {
-    constexpr int P = decltype(p)::value;
-    for (int kt = 0; kt < KTe - (NS - 1); ++kt) step(p, std::integral_constant<int, P>{}, kt + NS - 1);
-    for (int kt = KTe - (NS - 1); kt < KTe; ++kt)
-      step(p, std::integral_constant<int, P + 1>{}, kt + NS - 1 - KTe);
-  });
+    int cur = 0;       // stage read in this step
+    int nxt = NS - 1;  // stage refilled in this step
+    // One K step on pair p whose loads fetch slab k of pair Q.
+    auto step = [&](auto p, auto q_tag, int k) {
+      // Slabs of the next NS-1 steps are in flight; wait for this one only.
+      wait_vmcnt<L * (NS - 2)>();
+      // A plain s_barrier: __syncthreads() would add a release fence that
+      // waits for every outstanding load, including the slabs still allowed
+      // in flight. The empty asm statements keep the compiler from moving
+      // LDS accesses across the barrier.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // The slab NS-1 steps ahead goes to the stage last read in the
+      // previous step, which every wave has finished once past the barrier.
+      char* st = smem + nxt * C::STAGE_BYTES;
+      const char* As = smem + cur * C::STAGE_BYTES;
+      compute(p, As, As + C::A_BYTES, Plan{}, [&](auto kk) {
+        issue(q_tag, k, st, std::bool_constant<kk == Plan::A_AT>{}, std::bool_constant<kk == Plan::B_AT>{});
+      });
+      cur = cur + 1 == NS ? 0 : cur + 1;
+      nxt = nxt + 1 == NS ? 0 : nxt + 1;
+    };
+    static_for<0, C::NACC>([&](auto p) {
+      constexpr int P = decltype(p)::value;
+      for (int kt = 0; kt < KTe - (NS - 1); ++kt) step(p, std::integral_constant<int, P>{}, kt + NS - 1);
+      for (int kt = KTe - (NS - 1); kt < KTe; ++kt)
+        step(p, std::integral_constant<int, P + 1>{}, kt + NS - 1 - KTe);
+    });
+  }
   // Out-of-range loads still count; none may land after the epilogue
   // starts reusing this LDS.
   wait_vmcnt<0>();
   __syncthreads();
 
-  float* rowv = reinterpret_cast<float*>(smem + C::SCR_BYTES);
+  float* rowv = reinterpret_cast<float*>(smem + C::VEC_OFF);
   float* colv = rowv + C::BM;
   float* rowpart = colv + C::BN;  // [WN][BM]
   if constexpr (RSS) {
