@@ -77,9 +77,31 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kRowBytes = 128;  // bytes of K per staged tile row
-// Square tiles whose whole-slab stages fit only twice (256 x 256) stage
-// half-slabs in a ring of five instead (see the kernel's main loop).
-constexpr bool kHalfSlabRing = true;
+// Single-accumulator tiles whose whole-slab stages fit only twice (256 x 256,
+// 192 x 256, 256 x 192) stage each operand's K-step panels in a ring of its
+// own instead (see the kernel's main loop).
+constexpr bool kPanelRings = true;
+
+// Ring depths (A slots, B slots) for panels of a and b bytes in `cap`
+// bytes: the most panels in flight (all but the one being read of each
+// ring), at least two slots per ring; {0, 0} if none fits.
+struct RingDepth {
+  int na, nb;
+};
+constexpr RingDepth ring_depth(int a, int b, int cap) {
+  RingDepth best{0, 0};
+  int best_fl = -1;
+  for (int na = 2; na <= 8; ++na)
+    for (int nb = 2; nb <= 8; ++nb)
+      if (na * a + nb * b <= cap) {
+        const int fl = (na - 1) * a + (nb - 1) * b;
+        if (fl > best_fl || (fl == best_fl && na > best.na)) {
+          best = RingDepth{na, nb};
+          best_fl = fl;
+        }
+      }
+  return best;
+}
 
 __device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -184,10 +206,12 @@ struct Cfg {
   static constexpr int FIT_ = (160 * 1024 - VEC_BYTES_) / STAGE_BYTES;
   static constexpr int NSTAGE = FIT_ < 4 ? FIT_ : 4;
   static_assert(NSTAGE >= 2, "two pipeline stages must fit in LDS");
-  // Half-slab ring: five panels (an A or a B panel of one K step, A_BYTES
-  // each) fill the 160 KB, against two whole slabs plus the vectors.
-  static constexpr bool RING = kHalfSlabRing && BM == BN && NACC == 1 && NSTAGE == 2 && 5 * BM * RB <= 160 * 1024;
-  static constexpr int PIPE_BYTES = RING ? 5 * A_BYTES : NSTAGE * STAGE_BYTES;
+  // Panel rings: RA panels of A (A_BYTES each) and RB panels of B fill the
+  // 160 KB, against two whole slabs plus the vectors.
+  static constexpr RingDepth RD_ = ring_depth(A_BYTES, B_BYTES, 160 * 1024);
+  static constexpr bool RING = kPanelRings && NACC == 1 && NSTAGE == 2 && RD_.na > 0;
+  static constexpr int RA = RING ? RD_.na : 0, RBN = RING ? RD_.nb : 0;
+  static constexpr int PIPE_BYTES = RING ? RA * A_BYTES + RBN * B_BYTES : NSTAGE * STAGE_BYTES;
   // Epilogue staging: each wave writes 32 accumulator rows at a time (per
   // accumulator) into a private fp32 buffer with a row stride padded by 8
   // floats (the two half-waves of the MFMA layout then hit disjoint banks;
@@ -709,18 +733,25 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
     if constexpr (decltype(b_tag)::value) DB::issue(rb[Q], ldb_b[Q], k0, st + C::A_BYTES, wave, lane, oob);
   };
   if constexpr (C::RING) {
-    // Half-slab ring. K step k's panels are A_k and B_k; panel h of the
-    // sequence A_0, B_0, A_1, B_1, ... lives in slot h mod 5. Step k reads
-    // slots 2k, 2k+1 and issues B_{k+1} in its first sub-step (it is needed
-    // next) and A_{k+2} in its second, into slots 2k+3 and 2k+4 (mod 5):
-    // those held A_{k-1} and B_{k-1}, which every wave has finished once past
-    // the step's barrier. One and a half slabs stay in flight, against one
-    // with two whole-slab stages, and the wait at the top of a step lets the
-    // newest panel (A_{k+1}) stay outstanding. Issue order A_0, B_0, A_1,
-    // then two panels per step; with in-order completion, vmcnt(DA::INSTR)
-    // at the top of step k means A_k and B_k have landed.
-    static_assert(C::A_BYTES == C::B_BYTES && C::NACC == 1, "ring: square single-accumulator tiles");
-    constexpr int HB = C::A_BYTES;
+    // Panel rings. K step k's panels are A_k and B_k; A_k lives in slot
+    // k mod RA of the A ring and B_k in slot k mod RBN of the B ring. Step k
+    // reads A_k, B_k and issues A_{k+dA} and B_{k+dB} (dA = RA-1, dB =
+    // RBN-1) into the slots of A_{k-1} and B_{k-1}, which every wave has
+    // finished once past the step's barrier: all panels but the ones being
+    // read are in flight (one and a half to two slabs, against one with two
+    // whole-slab stages). Of the two loads of a step, the one due sooner
+    // goes first (first sub-step) and the other in the second. The prologue
+    // issues the same sequence for steps -max(dA,dB)..-1, skipping panels
+    // before index 0 (they all precede the later of A_0 and B_0), so with
+    // in-order completion, at the top of step k at most W loads issued
+    // after the later of A_k and B_k may be outstanding.
+    constexpr int NA = C::RA, NB = C::RBN, dA = NA - 1, dB = NB - 1;
+    constexpr bool aFirst = dA <= dB;
+    constexpr int W = dA == dB ? (dA - 1) * L
+                      : aFirst ? DB::INSTR + (dA - 1) * L : DA::INSTR + (dB - 1) * L;
+    constexpr int D = dA > dB ? dA : dB;
+    char* const ringA = smem;
+    char* const ringB = smem + NA * C::A_BYTES;
     auto panel = [&](auto is_a, int k, char* dst) {
       const bool live = k < KT;
       const uint32_t oob = live ? 0u : 0x80000000u;
@@ -730,25 +761,37 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
       if constexpr (decltype(is_a)::value) DA::issue(ra[0], lda_b[0], k0, dst, wave, lane, oob);
       else DB::issue(rb[0], ldb_b[0], k0, dst, wave, lane, oob);
     };
-    panel(std::true_type{}, 0, smem);
-    panel(std::false_type{}, 0, smem + HB);
-    panel(std::true_type{}, 1, smem + 2 * HB);
-    int h = 0;  // slot of A_k
+    static_for<0, D>([&](auto jj) {
+      constexpr int j = (int)jj - D;  // virtual step
+      constexpr int ka = j + dA, kb = j + dB;
+      if constexpr (aFirst) {
+        if constexpr (ka >= 0) panel(std::true_type{}, ka, ringA + ka * C::A_BYTES);
+        if constexpr (kb >= 0) panel(std::false_type{}, kb, ringB + kb * C::B_BYTES);
+      } else {
+        if constexpr (kb >= 0) panel(std::false_type{}, kb, ringB + kb * C::B_BYTES);
+        if constexpr (ka >= 0) panel(std::true_type{}, ka, ringA + ka * C::A_BYTES);
+      }
+    });
+    int sa = 0, sb = 0;  // slots of A_k, B_k
     const int KTr = KT > 1 ? KT : 1;
     for (int k = 0; k < KTr; ++k) {
-      wait_vmcnt<DA::INSTR>();
+      wait_vmcnt<W>();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const int hb = h == 4 ? 0 : h + 1;  // B_k
-      const int fb = h >= 2 ? h - 2 : h + 3;  // B_{k+1}
-      const int fa = h >= 1 ? h - 1 : h + 4;  // A_{k+2}
-      compute(std::integral_constant<int, 0>{}, smem + h * HB, smem + hb * HB, SlabPlan<DA::INSTR, 1, DB::INSTR, 0>{},
+      const int fa = sa == 0 ? NA - 1 : sa - 1;  // slot of A_{k-1}, refilled with A_{k+dA}
+      const int fb = sb == 0 ? NB - 1 : sb - 1;
+      char* const dstA = ringA + fa * C::A_BYTES;
+      char* const dstB = ringB + fb * C::B_BYTES;
+      typedef std::conditional_t<aFirst, SlabPlan<DA::INSTR, 0, DB::INSTR, 1>, SlabPlan<DA::INSTR, 1, DB::INSTR, 0>>
+          RPlan;
+      compute(std::integral_constant<int, 0>{}, ringA + sa * C::A_BYTES, ringB + sb * C::B_BYTES, RPlan{},
               [&](auto kk) {
-                if constexpr (kk == 0) panel(std::false_type{}, k + 1, smem + fb * HB);
-                else panel(std::true_type{}, k + 2, smem + fa * HB);
+                if constexpr (kk == RPlan::A_AT) panel(std::true_type{}, k + dA, dstA);
+                else panel(std::false_type{}, k + dB, dstB);
               });
-      h = h >= 3 ? h - 3 : h + 2;
+      sa = sa + 1 == NA ? 0 : sa + 1;
+      sb = sb + 1 == NB ? 0 : sb + 1;
     }
   } else {
     static_for<0, NS - 1>([&](auto s) {
