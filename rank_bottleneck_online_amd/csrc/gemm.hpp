@@ -41,9 +41,9 @@
 // Pipelining. As many LDS stages as fit (three or four for tiles smaller
 // than 256 x 256): while the MFMAs read stage kt, the slabs of the next
 // NSTAGE-1 steps are in flight, and each step waits only for the oldest.
-// 256 x 256 tiles, where two whole slabs fit, stage half-slabs (one
-// operand's panel of a K step) in a ring of five instead, which keeps one
-// and a half slabs in flight. The load instructions of the next slab are interleaved one by one
+// Single-accumulator tiles where only two whole slabs fit (256 x 256,
+// 192 x 256, 256 x 192) stage each operand's K-step panels in a ring of
+// its own instead, which keeps one and a half slabs or more in flight. The load instructions of the next slab are interleaved one by one
 // with the MFMAs of the first two k sub-steps, so that a stalled load issue
 // never leaves the matrix cores idle (with one wave per SIMD there is no
 // other wave to fill the gap). MFMA fragments are double-buffered across
