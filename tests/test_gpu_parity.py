@@ -78,14 +78,30 @@ def test_lrblock_global_width_divisor(B):
     compare_lrblock(out, inp, "bf16", "silu", True, d_norm=1024)
 
 
-def test_lrblock_parity_256x192_tiles(B):
+@pytest.mark.parametrize("d", [256, 64, 192])
+def test_lrblock_parity_256x192_tiles(B, d):
     # T = 4090, G r = 3072: 256 x 192 down tiles fill one round (16 x 16),
     # where 192 x 256 needs two (22 x 12) and 256 x 256 leaves a quarter of
     # the round idle, so the planner takes the 96-wide wave tiles whose
-    # epilogue reads back 12 lanes per row; ragged T.
-    T, d, r, G, n = 4090, 256, 1024, 3, 256
+    # epilogue reads back 12 lanes per row; ragged T. d = 64 and 192 give
+    # the down product one and three K steps, fewer than its B ring holds.
+    T, r, G, n = 4090, 1024, 3, 256
     say(f"lrblock 256x192 down tiles T={T} d={d} r={r} G={G} n={n} bf16 silu seed=4")
     inp = synth.lrblock_inputs(T, d, r, G, n, dtype="bf16", seed=4)
+    out = run_lrblock(B, inp, "bf16", "silu", True)
+    compare_lrblock(out, inp, "bf16", "silu", True)
+
+
+@pytest.mark.parametrize("r", [64, 128, 192])
+def test_lrblock_short_k_on_ring_tiles(B, r):
+    # T = 8190, n = d = 2048: the up product (K = r) and the input gradient
+    # (K = G r) run on 256 x 256 tiles, one full round, whose operand panels
+    # stream through the A and B rings; K = r of one, two and three K steps
+    # covers a loop shorter than the rings (panels past K are issued out of
+    # range and still counted). Ragged T.
+    T, d, G, n = 8190, 2048, 1, 2048
+    say(f"lrblock short-K ring tiles T={T} d={d} r={r} G={G} n={n} bf16 silu seed=5")
+    inp = synth.lrblock_inputs(T, d, r, G, n, dtype="bf16", seed=5)
     out = run_lrblock(B, inp, "bf16", "silu", True)
     compare_lrblock(out, inp, "bf16", "silu", True)
 
