@@ -45,13 +45,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without its comments and with whitespace runs collapsed:
+    what the compiler sees, so that edits to comments leave the digest of
+    the kernels unchanged."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_digest() -> str:
+    """Digest of the code of the library's sources and header (comments and
+    layout excluded), recorded with counter measurements so that they are
+    reported only while the kernels are unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_bottleneck_online_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    h.update(open(os.path.join(ROOT, "include", "boost_lrblock.h"), "rb").read())
+        h.update(code_text(open(os.path.join(csrc, f)).read()).encode())
+    h.update(code_text(open(os.path.join(ROOT, "include", "boost_lrblock.h")).read()).encode())
     return h.hexdigest()[:16]
 
 

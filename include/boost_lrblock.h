@@ -285,9 +285,12 @@ int boost_abi_version(void);                  /* BOOST_ABI_VERSION */
 /* ------------------------------------------------------------------------
  * Kernel timing (measurement support, off by default). While enabled, every
  * launch whose kernel label contains `name_filter` (all launches if NULL or
- * "") is bracketed by two hipEvents recorded on the launch stream. Events
- * are created here, up to max_records pairs; launches beyond that are not
- * timed. boost_profiler_report synchronises on the recorded events and
+ * "") is timed by a pair of hipEvents on the launch stream: a GEMM launch
+ * passes them to hipExtLaunchKernelGGL, which records them at the kernel's
+ * start and end (the timed span still includes the dispatch, a few
+ * microseconds); the element-wise passes record them around their launches.
+ * The events are timing-only (no system-scope fence). They are created
+ * here, up to max_records pairs; launches beyond that are not timed. boost_profiler_report synchronises on the recorded events and
  * writes one line per label, "label count total_ms", into buf (NUL
  * terminated, truncated to len). disable destroys the events. Not
  * thread-safe: enable, run, report and disable from one host thread.

@@ -172,6 +172,13 @@ def test_traffic_needs_the_calibration_copy(tmp_path):
         bench.traffic_json(fetch, write, "llama2_7b_mlp", 1024)
 
 
+def test_code_text_drops_comments_only():
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* the\n  answer */ }\n"
+    b = "int f(int x) {\n  return 2 * x;\n}\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(b.replace("2 *", "3 *"))
+
+
 def test_more_than_one_gpu_is_refused():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=120)
