@@ -309,6 +309,28 @@ struct DirectLoader {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + row0 * C::RB), 16, off, 0, 0, 0);
     }
   }
+  // The same loads with less per-load work, for loops that keep per-lane
+  // state: prepare() computes each instruction's lane offset once (row and
+  // swizzled chunk); issue_fast() adds the slab's K offset (one add per
+  // load, still range-checked), takes the LDS destination from a
+  // wave-uniform index (scalar), and sends a slab that is out of range
+  // through a resource of zero records instead of offsetting every lane.
+  __device__ __forceinline__ static void prepare(int64_t ld_bytes, int wave, int lane, uint32_t (&vo)[INSTR]) {
+#pragma unroll
+    for (int q = 0; q < INSTR; ++q) {
+      const int row = RPI * (q * C::NW + wave) + lane / C::CH;
+      vo[q] = (uint32_t)(row * ld_bytes) + (uint32_t)(((lane % C::CH) ^ lds_swz(row)) * 16);
+    }
+  }
+  __device__ __forceinline__ static void issue_fast(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t none, bool live,
+                                                    const uint32_t (&vo)[INSTR], int k0, char* tile, int wave_s) {
+    const __amdgpu_buffer_rsrc_t r = live ? rs : none;
+    const uint32_t koff = (uint32_t)(k0 * C::ES);
+#pragma unroll
+    for (int q = 0; q < INSTR; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(tile + RPI * (q * C::NW + wave_s) * C::RB), 16,
+                                               vo[q] + koff, 0, 0, 0);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -344,6 +366,25 @@ struct DirectLoaderMN {
       const uint32_t off = ((uint32_t)((k0 + row) * ld_bytes) + (uint32_t)(chunk * 16)) | oob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + row0 * RS), 16, off, 0, 0, 0);
     }
+  }
+  // As for the K-contiguous loader: lane offsets once, then one add of the
+  // slab's k-row offset per load.
+  __device__ __forceinline__ static void prepare(int64_t ld_bytes, int wave, int lane, uint32_t (&vo)[INSTR]) {
+#pragma unroll
+    for (int q = 0; q < INSTR; ++q) {
+      const int row = RPI * (q * C::NW + wave) + lane / CHR;
+      vo[q] = (uint32_t)(row * ld_bytes) + (uint32_t)(((lane % CHR) ^ mn_swz<C>(row)) * 16);
+    }
+  }
+  __device__ __forceinline__ static void issue_fast(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t none, bool live,
+                                                    const uint32_t (&vo)[INSTR], int k0, int64_t ld_bytes,
+                                                    char* __restrict__ tile, int wave_s) {
+    const __amdgpu_buffer_rsrc_t r = live ? rs : none;
+    const uint32_t koff = (uint32_t)(k0 * ld_bytes);
+#pragma unroll
+    for (int q = 0; q < INSTR; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(tile + RPI * (q * C::NW + wave_s) * RS), 16,
+                                               vo[q] + koff, 0, 0, 0);
   }
 };
 
@@ -752,14 +793,25 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
     constexpr int D = dA > dB ? dA : dB;
     char* const ringA = smem;
     char* const ringB = smem + NA * C::A_BYTES;
+    // Loads with per-lane offsets computed once (see the loaders'
+    // issue_fast); a panel past K goes through a resource of zero records.
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t voA[DA::INSTR], voB[DB::INSTR];
+    DA::prepare(lda_b[0], wave, lane, voA);
+    DB::prepare(ldb_b[0], wave, lane, voB);
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(ops.a[0].ptr, 0);
     auto panel = [&](auto is_a, int k, char* dst) {
       const bool live = k < KT;
-      const uint32_t oob = live ? 0u : 0x80000000u;
       int kr = k + krot;
       kr = kr >= KT ? kr - KT : kr;
       const int k0 = kbeg + (live ? kr : 0) * C::BK;
-      if constexpr (decltype(is_a)::value) DA::issue(ra[0], lda_b[0], k0, dst, wave, lane, oob);
-      else DB::issue(rb[0], ldb_b[0], k0, dst, wave, lane, oob);
+      if constexpr (decltype(is_a)::value) {
+        if constexpr (C::AKC) DA::issue_fast(ra[0], none, live, voA, k0, dst, wave_s);
+        else DA::issue_fast(ra[0], none, live, voA, k0, lda_b[0], dst, wave_s);
+      } else {
+        if constexpr (C::BKC) DB::issue_fast(rb[0], none, live, voB, k0, dst, wave_s);
+        else DB::issue_fast(rb[0], none, live, voB, k0, ldb_b[0], dst, wave_s);
+      }
     };
     static_for<0, D>([&](auto jj) {
       constexpr int j = (int)jj - D;  // virtual step
