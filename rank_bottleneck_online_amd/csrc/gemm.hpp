@@ -388,6 +388,36 @@ struct DirectLoaderMN {
   }
 };
 
+// Whole-slab loads with the loaders' prepared lane offsets: the offsets of
+// every operand pair, computed once per lane, and the slab issue that adds
+// the K offset.
+template <class C, class DA, class DB>
+struct SlabLoads {
+  uint32_t va[C::NACC][DA::INSTR], vb[C::NACC][DB::INSTR];
+  __device__ __forceinline__ void prepare(const int64_t (&lda)[C::NACC], const int64_t (&ldb)[C::NACC], int wave,
+                                          int lane) {
+#pragma unroll
+    for (int p = 0; p < C::NACC; ++p) {
+      DA::prepare(lda[p], wave, lane, va[p]);
+      DB::prepare(ldb[p], wave, lane, vb[p]);
+    }
+  }
+  template <int Q, bool LA, bool LB>
+  __device__ __forceinline__ void issue(const __amdgpu_buffer_rsrc_t (&ra)[C::NACC],
+                                        const __amdgpu_buffer_rsrc_t (&rb)[C::NACC], __amdgpu_buffer_rsrc_t none,
+                                        const int64_t (&lda)[C::NACC], const int64_t (&ldb)[C::NACC], bool live,
+                                        int k0, char* st, int wave_s) const {
+    if constexpr (LA) {
+      if constexpr (C::AKC) DA::issue_fast(ra[Q], none, live, va[Q], k0, st, wave_s);
+      else DA::issue_fast(ra[Q], none, live, va[Q], k0, lda[Q], st, wave_s);
+    }
+    if constexpr (LB) {
+      if constexpr (C::BKC) DB::issue_fast(rb[Q], none, live, vb[Q], k0, st + C::A_BYTES, wave_s);
+      else DB::issue_fast(rb[Q], none, live, vb[Q], k0, ldb[Q], st + C::A_BYTES, wave_s);
+    }
+  }
+};
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
@@ -762,16 +792,30 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
   // rotated order; the order is fixed for a given problem, so results stay
   // bit-reproducible.
   const int krot = KT > 0 ? (int)((((blockIdx.x & 7u) * (unsigned)KT * (unsigned)g.krot) >> 4) % (unsigned)KT) : 0;
+  // Whole-slab loads of tiles with one or two accumulators use the
+  // loaders' prepared lane offsets (as the panel rings do); the
+  // three-accumulator tile, at the edge of the register file, computes them
+  // per load.
+  constexpr bool kFastSlab = !C::RING && C::NACC <= 2 && C::ES == 2;
+  SlabLoads<C, DA, DB> fast;
+  if constexpr (kFastSlab) fast.prepare(lda_b, ldb_b, wave, lane);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const __amdgpu_buffer_rsrc_t none_s = make_rsrc(ops.a[0].ptr, 0);
   auto issue = [&](auto q_tag, int k, char* st, auto a_tag, auto b_tag) {
     constexpr int Q = decltype(q_tag)::value < C::NACC ? decltype(q_tag)::value : 0;
     constexpr bool past = decltype(q_tag)::value >= C::NACC;
     const bool live = !past && k < KT;
-    const uint32_t oob = live ? 0u : 0x80000000u;
     int kr = k + krot;
     kr = kr >= KT ? kr - KT : kr;
     const int k0 = kbeg + (live ? kr : 0) * C::BK;
-    if constexpr (decltype(a_tag)::value) DA::issue(ra[Q], lda_b[Q], k0, st, wave, lane, oob);
-    if constexpr (decltype(b_tag)::value) DB::issue(rb[Q], ldb_b[Q], k0, st + C::A_BYTES, wave, lane, oob);
+    if constexpr (kFastSlab) {
+      fast.template issue<Q, decltype(a_tag)::value, decltype(b_tag)::value>(ra, rb, none_s, lda_b, ldb_b, live, k0, st,
+                                                                             wave_u);
+    } else {
+      const uint32_t oob = live ? 0u : 0x80000000u;
+      if constexpr (decltype(a_tag)::value) DA::issue(ra[Q], lda_b[Q], k0, st, wave, lane, oob);
+      if constexpr (decltype(b_tag)::value) DB::issue(rb[Q], ldb_b[Q], k0, st + C::A_BYTES, wave, lane, oob);
+    }
   };
   if constexpr (C::RING) {
     // Panel rings. K step k's panels are A_k and B_k; A_k lives in slot
