@@ -57,6 +57,8 @@ LRBLOCK_CASES = [
     (257, 384, 128, 1, 384, "bf16", "silu", False),     # O-projection form
     (1, 256, 64, 3, 128, "bf16", "silu", True),         # a single token
     (640, 1024, 256, 2, 1024, "bf16", "silu", True),
+    (130, 256, 64, 16, 128, "bf16", "silu", True),     # the most groups a descriptor takes
+    (70, 128, 64, 16, 64, "f32", "identity", True),
 ]
 
 
