@@ -792,15 +792,17 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
   // rotated order; the order is fixed for a given problem, so results stay
   // bit-reproducible.
   const int krot = KT > 0 ? (int)((((blockIdx.x & 7u) * (unsigned)KT * (unsigned)g.krot) >> 4) % (unsigned)KT) : 0;
-  // Whole-slab loads of tiles with one or two accumulators use the
-  // loaders' prepared lane offsets (as the panel rings do); the
-  // three-accumulator tile, at the edge of the register file, computes them
-  // per load.
+  // Loads with per-lane offsets computed once (the loaders' prepare() and
+  // issue_fast()): a wave-uniform copy of the wave index for the LDS
+  // destinations, and a resource of zero records for panels past K. The
+  // panel rings and the whole-slab pipeline of tiles with one or two
+  // accumulators use them; the three-accumulator tile, at the edge of the
+  // register file, computes its offsets per load.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const __amdgpu_buffer_rsrc_t none_s = make_rsrc(ops.a[0].ptr, 0);
   constexpr bool kFastSlab = !C::RING && C::NACC <= 2 && C::ES == 2;
   SlabLoads<C, DA, DB> fast;
   if constexpr (kFastSlab) fast.prepare(lda_b, ldb_b, wave, lane);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const __amdgpu_buffer_rsrc_t none_s = make_rsrc(ops.a[0].ptr, 0);
   auto issue = [&](auto q_tag, int k, char* st, auto a_tag, auto b_tag) {
     constexpr int Q = decltype(q_tag)::value < C::NACC ? decltype(q_tag)::value : 0;
     constexpr bool past = decltype(q_tag)::value >= C::NACC;
@@ -837,24 +839,20 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
     constexpr int D = dA > dB ? dA : dB;
     char* const ringA = smem;
     char* const ringB = smem + NA * C::A_BYTES;
-    // Loads with per-lane offsets computed once (see the loaders'
-    // issue_fast); a panel past K goes through a resource of zero records.
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     uint32_t voA[DA::INSTR], voB[DB::INSTR];
     DA::prepare(lda_b[0], wave, lane, voA);
     DB::prepare(ldb_b[0], wave, lane, voB);
-    const __amdgpu_buffer_rsrc_t none = make_rsrc(ops.a[0].ptr, 0);
     auto panel = [&](auto is_a, int k, char* dst) {
       const bool live = k < KT;
       int kr = k + krot;
       kr = kr >= KT ? kr - KT : kr;
       const int k0 = kbeg + (live ? kr : 0) * C::BK;
       if constexpr (decltype(is_a)::value) {
-        if constexpr (C::AKC) DA::issue_fast(ra[0], none, live, voA, k0, dst, wave_s);
-        else DA::issue_fast(ra[0], none, live, voA, k0, lda_b[0], dst, wave_s);
+        if constexpr (C::AKC) DA::issue_fast(ra[0], none_s, live, voA, k0, dst, wave_u);
+        else DA::issue_fast(ra[0], none_s, live, voA, k0, lda_b[0], dst, wave_u);
       } else {
-        if constexpr (C::BKC) DB::issue_fast(rb[0], none, live, voB, k0, dst, wave_s);
-        else DB::issue_fast(rb[0], none, live, voB, k0, ldb_b[0], dst, wave_s);
+        if constexpr (C::BKC) DB::issue_fast(rb[0], none_s, live, voB, k0, dst, wave_u);
+        else DB::issue_fast(rb[0], none_s, live, voB, k0, ldb_b[0], dst, wave_u);
       }
     };
     static_for<0, D>([&](auto jj) {
