@@ -84,7 +84,9 @@ constexpr bool kPanelRings = true;
 
 // Ring depths (A slots, B slots) for panels of a and b bytes in `cap`
 // bytes: the most panels in flight (all but the one being read of each
-// ring), at least two slots per ring; {0, 0} if none fits.
+// ring), at least two slots per ring; {0, 0} if none fits. On a tie the B
+// ring gets the extra slot (measured on the 256 x 256 tiles, 2 + 3 against
+// 3 + 2 slots: the 7B MLP step 0.8-1.1% faster, the 40B layer 0.4-0.5%).
 struct RingDepth {
   int na, nb;
 };
@@ -95,7 +97,7 @@ constexpr RingDepth ring_depth(int a, int b, int cap) {
     for (int nb = 2; nb <= 8; ++nb)
       if (na * a + nb * b <= cap) {
         const int fl = (na - 1) * a + (nb - 1) * b;
-        if (fl > best_fl || (fl == best_fl && na > best.na)) {
+        if (fl > best_fl || (fl == best_fl && nb > best.nb)) {
           best = RingDepth{na, nb};
           best_fl = fl;
         }
