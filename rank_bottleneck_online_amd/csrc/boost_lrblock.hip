@@ -132,11 +132,12 @@ struct Choice {
 };
 
 // K rotation by XCD (eighths of the loop per XCD index) for loops of at
-// least 4096. Measured: isolated long-K 256 x 256 products 12-20% faster,
-// short loops (K = 1024) slower; on the whole workloads, the 7B MLP step
-// -0.9%, the 1B QKV forward -2%, the 40B layer and 13B share unchanged,
-// against no rotation or rotation of the 256 x 256 tile only.
-int krot_rule(CfgId, int64_t k_split) { return k_split >= 4096 ? 2 : 0; }
+// least 1024. Measured: isolated long-K 256 x 256 products 12-20% faster;
+// on the whole workloads, rotating loops of 4096 or more made the 7B MLP
+// step 0.9% and the 1B QKV forward 2% faster (the 40B layer and 13B share
+// unchanged) against no rotation; extending it to loops of 1024 (the K = r
+// products) took another 0.3-0.7% off the 7B step, the others unchanged.
+int krot_rule(CfgId, int64_t k_split) { return k_split >= 1024 ? 2 : 0; }
 
 // Pick the tile shape (and, where a product writes fp32 partials that a
 // reduction can sum, the number of K splits) minimising a simple model:
