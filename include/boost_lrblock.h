@@ -238,8 +238,9 @@ int boost_lrmlp_bwd_chained(const boost_lrmlp_desc* desc, const void* x, const v
 
 /* Attention stand-in between a layer's QKV and O blocks (the attention core
  * is not part of the bottleneck block): a[T,d] = q + k + v for qkv[3,T,d]
- * (dtype; summed in fp32, one rounding), and its backward
- * dqkv[3,T,d] = (da, da, da). d must be a multiple of 64. */
+ * (dtype; summed exactly in fp64, then rounded to fp32 and, for bf16, from
+ * there to bf16), and its backward dqkv[3,T,d] = (da, da, da). d must be a
+ * multiple of 64. */
 int boost_attn_standin_fwd(int dtype, int64_t T, int64_t d, const void* qkv, void* a, void* stream);
 int boost_attn_standin_bwd(int dtype, int64_t T, int64_t d, const void* da, void* dqkv, void* stream);
 

@@ -219,8 +219,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4* __rest
 }
 
 // Attention stand-in (the attention core is not part of the block): a =
-// q + k + v elementwise over qkv[3][n] (fp32 sum, one rounding), and its
-// gradient, dq = dk = dv = da. n is a multiple of 8; 16-byte accesses.
+// q + k + v elementwise over qkv[3][n], and its gradient, dq = dk = dv = da.
+// The sum is taken in fp64, where it is exact for any three bf16 values
+// within 2^43 of each other (an fp32 sum of two of them first is not: it
+// rounds when their exponents differ by more than 16), then rounded to fp32
+// and stored like every other fp32 result (bf16: round to nearest even from
+// that fp32 value). The bf16 rounding is done on the fp32 bits: a plain
+// conversion chain double -> float -> bf16 is compiled into one rounding
+// straight from the double, which differs where the fp32 value is a bf16
+// tie. Finite values. n is a multiple of 8; 16-byte accesses.
 template <typename T>
 __global__ __launch_bounds__(256) void standin_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ a, int64_t n) {
   constexpr int VEC = 16 / sizeof(T);
@@ -231,15 +238,22 @@ __global__ __launch_bounds__(256) void standin_fwd_kernel(const T* __restrict__ 
       Vec8<bf16>::load(qkv, i, q);
       Vec8<bf16>::load(qkv, n + i, k);
       Vec8<bf16>::load(qkv, 2 * n + i, v);
+      uint32_t h[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] += k[e] + v[e];
-      Vec8<bf16>::store(a, i, q);
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)((double)q[e] + (double)k[e] + (double)v[e]);
+        const uint32_t b = __builtin_bit_cast(uint32_t, f);
+        h[e] = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+      }
+      *reinterpret_cast<u32x4*>(a + i) =
+          u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     } else {
       const float4 x = *reinterpret_cast<const float4*>(qkv + i);
       const float4 y = *reinterpret_cast<const float4*>(qkv + n + i);
       const float4 z = *reinterpret_cast<const float4*>(qkv + 2 * n + i);
-      *reinterpret_cast<float4*>(a + i) = make_float4(x.x + y.x + z.x, x.y + y.y + z.y, x.z + y.z + z.z,
-                                                      x.w + y.w + z.w);
+      auto sum3 = [](float p, float q, float r) { return (float)((double)p + (double)q + (double)r); };
+      *reinterpret_cast<float4*>(a + i) =
+          make_float4(sum3(x.x, y.x, z.x), sum3(x.y, y.y, z.y), sum3(x.z, y.z, z.z), sum3(x.w, y.w, z.w));
     }
   }
 }

@@ -82,7 +82,7 @@ def check_blocks_on_their_inputs(out, inp, act):
     # QKV block
     fq = oracle.lrblock_forward(inp["x"], q["g"], q["A_cat"], q["B"], act)
     check("sumsq_x", host(out["sumsq_x"]), fq["sumsq"], "bf16")
-    # stand-in: a = q + k + v is exact in fp32 before its one rounding
+    # stand-in: a = q + k + v, summed exactly, then rounded to fp32 and bf16
     qkv = host(out["qkv"])
     assert np.array_equal(host(out["a"]), rnd(oracle.standin_forward(qkv)))
     # O block with the residual and the next statistic

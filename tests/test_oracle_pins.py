@@ -389,3 +389,16 @@ def test_bf16_rounding_ties_to_even():
     # the even significand (1); 1 + 3*2^-8 ties up to 1 + 2^-6.
     v = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -30])
     np.testing.assert_array_equal(synth.round_to_bf16(v), [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7])
+
+
+def test_stored_results_round_through_fp32():
+    # A stored result is the fp32 value rounded to bf16, as a device stores
+    # its fp32 results. The stand-in sum -1.0703125 - (2^-26 + 2^-28) -
+    # 0.35546875 lies 1.86e-8 beyond the bf16 midpoint -1.42578125; that is
+    # under half an fp32 ulp (5.96e-8), so fp32 holds the midpoint itself and
+    # the tie goes to the even neighbour -1.421875 (a single rounding of the
+    # exact sum would give -1.4296875).
+    qkv = np.array([[[-1.0703125]], [[-(2.0 ** -26 + 2.0 ** -28)]], [[-0.35546875]]])
+    s = oracle.standin_forward(qkv)
+    assert s[0, 0] == -1.0703125 - (2.0 ** -26 + 2.0 ** -28) - 0.35546875
+    assert oracle.round_to_bf16(s)[0, 0] == -1.421875
