@@ -254,6 +254,7 @@ struct GemmGeom {
   int k_split;   // K range per split, a multiple of BK
   int tiles_m, tiles_n;
   int krot;      // the workgroups of XCD x start their K loops krot * x / 16 of the way in
+  int group;     // tile rows per group of the tile walk
 };
 
 struct GemmOps {
@@ -479,16 +480,15 @@ struct SlabPlan {
 // ---------------------------------------------------------------------------
 // Block -> tile mapping. Workgroups are handed to the 8 XCDs round-robin;
 // the remap gives each XCD a contiguous range of logical tiles, and tiles are
-// walked in groups of 8 tile rows so neighbours share A rows and B columns in
-// that XCD's L2.
+// walked in groups of GROUP tile rows (chosen per launch) so neighbours share
+// A rows and B columns in that XCD's L2.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   const int q = nb >> 3, rem = nb & 7, x = b & 7;
   return x * q + (x < rem ? x : rem) + (b >> 3);
 }
 
-__device__ __forceinline__ void group_tile(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int GROUP = 8;
+__device__ __forceinline__ void group_tile(int tile, int tiles_m, int tiles_n, int GROUP, int& tm, int& tn) {
   const int per_group = GROUP * tiles_n;
   const int gid = tile / per_group;
   const int first = gid * GROUP;
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmGeom g, GemmOps ops, ty
   const int tiles = g.tiles_m * g.tiles_n;
   const int prob = bid / tiles;
   int tm, tn;
-  group_tile(bid - prob * tiles, g.tiles_m, g.tiles_n, tm, tn);
+  group_tile(bid - prob * tiles, g.tiles_m, g.tiles_n, g.group, tm, tn);
   const int split = prob % g.splits, bidx = prob / g.splits;
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int kbeg = split * g.k_split;
